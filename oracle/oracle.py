@@ -1,0 +1,348 @@
+"""Python front end of the fp64 CPU oracle (``oracle.c``) and a second,
+independent NumPy dense-mask formulation of the same path.
+
+TEST INFRASTRUCTURE ONLY: only the tests, the smoke check and the benchmark's
+CPU-baseline leg may import this module.  It never imports the HIP package and
+the HIP package never imports it.
+
+Sources: "DeepSeek-V4-Pro 架构：一个 token 的旅程" (hs-black.github.io) and
+"图解DeepSeek V4：详细计算流程解析" (jsqmd.com); the C file names the sections each
+function follows.
+
+Input arrays may be float32, float64, or uint16 holding bf16 bit patterns;
+they are widened exactly inside the C code.  Outputs are float64.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# A different build of this same file may be substituted (mutation checks of the pins).
+_LIB_OVERRIDE = os.environ.get("CSA_ORACLE_LIB")
+
+F32, BF16, F64 = 0, 1, 2
+NO_RELU = 1
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c into liboracle.so (plain gcc, OpenMP over queries)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", "-std=c11", _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if _LIB_OVERRIDE:
+            L = ctypes.CDLL(_LIB_OVERRIDE)
+        else:
+            if not os.path.exists(_LIB_PATH):
+                build(force=True)
+            L = ctypes.CDLL(_LIB_PATH)
+        vp, i32, dbl = ctypes.c_void_p, ctypes.c_int, ctypes.c_double
+        L.orc_rope.argtypes = [vp, i32, dbl, dbl, i32]
+        L.orc_pool.argtypes = [vp, vp, i32, i32, i32, i32, i32, ctypes.c_long, ctypes.c_long, vp]
+        L.orc_pool.restype = i32
+        L.orc_compress.argtypes = [vp, vp, i32, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, dbl, dbl]
+        L.orc_compress.restype = ctypes.c_long
+        L.orc_compress_rolling.argtypes = [vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32, dbl, dbl]
+        L.orc_compress_rolling.restype = ctypes.c_long
+        L.orc_index_scores.argtypes = [vp, i32, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32, ctypes.c_uint, vp, vp]
+        L.orc_topk.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp]
+        L.orc_attn.argtypes = [vp, i32, vp, i32, vp, i32, i32, vp, i32, vp, vp, vp, vp, vp, vp,
+                               i32, i32, i32, i32, i32, i32, i32, i32, dbl, dbl]
+        L.orc_attn.restype = i32
+        _lib = L
+    return _lib
+
+
+def _dt(a: np.ndarray) -> int:
+    if a.dtype == np.float32:
+        return F32
+    if a.dtype == np.float64:
+        return F64
+    if a.dtype == np.uint16:
+        return BF16
+    raise TypeError(f"unsupported oracle input dtype {a.dtype}")
+
+
+def _c(a: np.ndarray) -> np.ndarray:
+    return np.ascontiguousarray(a)
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+# --------------------------------------------------------------------------
+def rope(x: np.ndarray, pos: float, base: float = 10000.0, inverse: bool = False) -> np.ndarray:
+    """RoPE of a 1-D vector x (the whole vector is the rotated part)."""
+    y = np.array(x, dtype=np.float64, copy=True)
+    lib().orc_rope(_p(y), y.shape[0], float(pos), float(base), -1 if inverse else 1)
+    return y
+
+
+def pool(kv, sc, d, ratio, overlap, pos0, g):
+    """Pooled entry g (before RMSNorm) of one sequence; kv, sc: [L, m*d]."""
+    kv, sc = _c(kv), _c(sc)
+    assert kv.dtype == sc.dtype
+    out = np.zeros(d, dtype=np.float64)
+    rc = lib().orc_pool(_p(kv), _p(sc), _dt(kv), kv.shape[0], d, ratio, int(overlap), int(pos0), int(g), _p(out))
+    if rc != 0:
+        raise ValueError("group not fully inside the state buffer")
+    return out
+
+
+def compress(kv_state, score_state, gamma, pos0, ratio, overlap, N_cap, rope_dim, cache=None,
+             eps=1e-6, rope_base=10000.0):
+    """Parallel-form compressor.  Returns (cache f64 [B,N_cap,d], written bool [B,N_cap])."""
+    kv_state, score_state = _c(kv_state), _c(score_state)
+    B, L, md = kv_state.shape
+    d = md // (2 if overlap else 1)
+    if cache is None:
+        cache = np.zeros((B, N_cap, d), dtype=np.float64)
+    else:
+        cache = np.array(cache, dtype=np.float64, copy=True)
+    written = np.zeros((B, N_cap), dtype=np.uint8)
+    g64 = _c(np.asarray(gamma, dtype=np.float64))
+    p0 = _c(np.asarray(pos0, dtype=np.int32))
+    lib().orc_compress(_p(kv_state), _p(score_state), _dt(kv_state), _p(g64), _p(cache), _p(written), _p(p0),
+                       B, L, d, rope_dim, ratio, int(overlap), N_cap, float(eps), float(rope_base))
+    return cache, written.astype(bool)
+
+
+def compress_rolling(kv_state, score_state, gamma, ratio, N_cap, rope_dim, eps=1e-6, rope_base=10000.0):
+    """Literal rolling-state (concat + roll) form; sequences start at position 0."""
+    kv_state, score_state = _c(kv_state), _c(score_state)
+    B, L, md = kv_state.shape
+    d = md // 2
+    cache = np.zeros((B, N_cap, d), dtype=np.float64)
+    g64 = _c(np.asarray(gamma, dtype=np.float64))
+    lib().orc_compress_rolling(_p(kv_state), _p(score_state), _dt(kv_state), _p(g64), _p(cache), B, L, d,
+                               rope_dim, ratio, N_cap, float(eps), float(rope_base))
+    return cache
+
+
+def index_scores(q_idx, w, idx_cache, q_pos, ratio, relu=True):
+    """Scores [B,S,N_cap] (-inf past the visible count) and nvis [B,S]."""
+    q_idx, idx_cache = _c(q_idx), _c(idx_cache)
+    B, S, Hi, di = q_idx.shape
+    N_cap = idx_cache.shape[1]
+    w64 = _c(np.asarray(w, dtype=np.float64).reshape(B, S, Hi))
+    qp = _c(np.asarray(q_pos, dtype=np.int32))
+    scores = np.empty((B, S, N_cap), dtype=np.float64)
+    nvis = np.empty((B, S), dtype=np.int32)
+    lib().orc_index_scores(_p(q_idx), _dt(q_idx), _p(w64), _p(idx_cache), _dt(idx_cache), _p(qp), B, S, Hi, di,
+                           N_cap, ratio, 0 if relu else NO_RELU, _p(scores), _p(nvis))
+    return scores, nvis
+
+
+def topk(scores, nvis, k):
+    """Indices [B,S,k] (descending score, ties to lower index, -1 padded) and k-th score [B,S]."""
+    scores = _c(np.asarray(scores, dtype=np.float64))
+    nvis = _c(np.asarray(nvis, dtype=np.int32))
+    B, S, N_cap = scores.shape
+    idx = np.empty((B, S, k), dtype=np.int32)
+    kth = np.empty((B, S), dtype=np.float64)
+    lib().orc_topk(_p(scores), _p(nvis), B, S, N_cap, k, _p(idx), _p(kth))
+    return idx, kth
+
+
+def attn(q, cmp_cache, win_kv, sink, q_pos, *, topk_idx=None, ratio=4, win_pos0=None, window=128,
+         rope_dim=64, scale=None, rope_base=10000.0):
+    """Sparse (topk_idx given) or dense (topk_idx None: all visible entries) MQA with sink.
+
+    Returns (out f64 [B,S,H,D], lse [B,S,H], ncand [B,S])."""
+    q, cmp_cache, win_kv = _c(q), _c(cmp_cache), _c(win_kv)
+    B, S, H, D = q.shape
+    N_cap = cmp_cache.shape[1]
+    W_cap = win_kv.shape[1]
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    s64 = _c(np.asarray(sink, dtype=np.float64))
+    qp = _c(np.asarray(q_pos, dtype=np.int32))
+    k = 0
+    ti = None
+    if topk_idx is not None:
+        ti = _c(np.asarray(topk_idx, dtype=np.int32))
+        k = ti.shape[-1]
+    wp = None if win_pos0 is None else _c(np.asarray(win_pos0, dtype=np.int32))
+    out = np.empty((B, S, H, D), dtype=np.float64)
+    lse = np.empty((B, S, H), dtype=np.float64)
+    ncand = np.empty((B, S), dtype=np.int32)
+    rc = lib().orc_attn(_p(q), _dt(q), _p(cmp_cache), _dt(cmp_cache), _p(ti), k, ratio, _p(win_kv), _dt(win_kv),
+                        _p(wp), _p(s64), _p(qp), _p(out), _p(lse), _p(ncand), B, S, H, D, rope_dim, N_cap, W_cap,
+                        window, float(scale), float(rope_base))
+    if rc != 0:
+        raise ValueError("a window row lies outside the window buffer")
+    return out, lse, ncand
+
+
+# --------------------------------------------------------------------------
+# Second formulation: dense masks over whole sequences, no gathers.  Used to
+# cross-check the C oracle on small inputs.
+# --------------------------------------------------------------------------
+def _f64(a):
+    a = np.asarray(a)
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def _rope_mat(x, pos, rope_dim, base, sign):
+    """Rotate the last rope_dim entries of x[..., D] at per-row positions pos[...]."""
+    x = np.array(x, dtype=np.float64, copy=True)
+    if rope_dim == 0:
+        return x
+    i = np.arange(rope_dim // 2, dtype=np.float64)
+    theta = sign * np.asarray(pos, dtype=np.float64)[..., None] * base ** (-2.0 * i / rope_dim)
+    tail = x[..., x.shape[-1] - rope_dim:]
+    a, b = tail[..., 0::2].copy(), tail[..., 1::2].copy()
+    tail[..., 0::2] = a * np.cos(theta) - b * np.sin(theta)
+    tail[..., 1::2] = a * np.sin(theta) + b * np.cos(theta)
+    return x
+
+
+def dense_pipeline(inp: dict) -> dict:
+    """Whole CSA (or HCA when inp['hca']) path for sequences that start at
+    position 0 and are queried causally at every token, via dense masks."""
+    kv = _f64(inp["kv_state"])          # [B, T, m*d]
+    sc = _f64(inp["score_state"])
+    B, T, md = kv.shape
+    ratio, overlap = inp["ratio"], inp["overlap"]
+    d = md // (2 if overlap else 1)
+    rope_dim, base, eps = inp["rope_dim"], inp.get("rope_base", 10000.0), inp.get("eps", 1e-6)
+    G = T // ratio
+    tok = np.arange(T)
+
+    def entries(kv, sc, d, gamma, rope_dim):
+        out = np.zeros((B, G, d))
+        for g in range(G):
+            own = (tok // ratio) == g
+            prev = (tok // ratio) == g - 1
+            if overlap:
+                s_all = np.concatenate([np.where(prev[None, :, None], sc[:, :, :d], -np.inf),
+                                        np.where(own[None, :, None], sc[:, :, d:], -np.inf)], axis=1)
+                v_all = np.concatenate([kv[:, :, :d], kv[:, :, d:]], axis=1)
+            else:
+                s_all = np.where(own[None, :, None], sc, -np.inf)
+                v_all = kv
+            wgt = np.exp(s_all - s_all.max(axis=1, keepdims=True))
+            wgt = wgt / wgt.sum(axis=1, keepdims=True)
+            pooled = (wgt * np.where(np.isfinite(s_all), v_all, 0.0)).sum(axis=1)
+            y = pooled / np.sqrt((pooled ** 2).mean(axis=-1, keepdims=True) + eps) * np.asarray(gamma)
+            out[:, g] = _rope_mat(y, np.full((B,), g * ratio), rope_dim, base, +1)
+        return out
+
+    cache = entries(kv, sc, d, inp["gamma"], rope_dim)
+    q = _f64(inp["q"])                 # [B, T, H, D]
+    win = _f64(inp["win_kv"])          # [B, T, D] linear rows for positions 0..T-1
+    H = q.shape[2]
+    t = tok
+    nvis = (t + 1) // ratio            # [T]
+    vis = np.arange(G)[None, :] < nvis[:, None]          # [T, G]
+    res = {"cache": cache}
+    if not inp.get("hca", False):
+        ikv, isc = _f64(inp["idx_kv_state"]), _f64(inp["idx_score_state"])
+        di = ikv.shape[-1] // 2
+        icache = entries(ikv, isc, di, inp["idx_gamma"], inp["idx_rope_dim"])
+        qi = _f64(inp["q_idx"])        # [B, T, Hi, di]
+        w = np.asarray(inp["w"], dtype=np.float64)       # [B, T, Hi]
+        dots = np.einsum("bthc,bgc->bthg", qi, icache)
+        score = np.einsum("bth,bthg->btg", w, np.maximum(dots, 0.0))
+        score = np.where(vis[None], score, -np.inf)
+        k = inp["k"]
+        sel = np.zeros((B, T, G), dtype=bool)
+        for b in range(B):
+            for tt in range(T):
+                order = np.argsort(-score[b, tt], kind="stable")[: min(k, nvis[tt])]
+                sel[b, tt, order] = True
+        res["icache"], res["scores"], res["sel"] = icache, score, sel
+        cmp_mask = sel
+    else:
+        cmp_mask = np.broadcast_to(vis[None], (B, T, G))
+    window = inp["window"]
+    win_mask = (tok[None, :] <= t[:, None]) & (tok[None, :] > t[:, None] - window)   # [T, T]
+    keys = np.concatenate([win, cache], axis=1)                                        # [B, T+G, D]
+    mask = np.concatenate([np.broadcast_to(win_mask[None], (B, T, T)), cmp_mask], axis=2)  # [B, T, T+G]
+    D = q.shape[-1]
+    scale = inp.get("scale", 1.0 / np.sqrt(D))
+    logits = scale * np.einsum("bthc,bjc->bthj", q, keys)
+    logits = np.where(mask[:, :, None, :], logits, -np.inf)
+    sink = np.asarray(inp["sink"], dtype=np.float64)
+    mx = np.maximum(logits.max(axis=-1), sink[None, None, :])
+    e = np.exp(logits - mx[..., None])
+    Z = e.sum(axis=-1) + np.exp(sink[None, None, :] - mx)
+    o = np.einsum("bthj,bjc->bthc", e / Z[..., None], keys)
+    res["out"] = _rope_mat(o, np.broadcast_to(t[None, :, None], o.shape[:3]), rope_dim, base, -1)
+    res["lse"] = mx + np.log(Z)
+    return res
+
+
+# --------------------------------------------------------------------------
+# Stage composition (C oracle)
+# --------------------------------------------------------------------------
+def _store_like(raw: np.ndarray, values64: np.ndarray) -> np.ndarray:
+    """Round fp64 values to the storage type of ``raw`` (bf16 bits: via fp32,
+    nearest-even; fp32: nearest)."""
+    f = np.asarray(values64, dtype=np.float64).astype(np.float32)
+    if raw.dtype == np.uint16:
+        u = f.view(np.uint32)
+        return ((u + ((u >> 16) & 1) + np.uint32(0x7FFF)) >> 16).astype(np.uint16)
+    if raw.dtype == np.float32:
+        return f
+    return np.asarray(values64, dtype=np.float64)
+
+
+def widen(raw: np.ndarray) -> np.ndarray:
+    return _f64(raw)
+
+
+def compress_into(raw_cache, kv_state, score_state, gamma, pos0, ratio, overlap, rope_dim, eps=1e-6,
+                  rope_base=10000.0):
+    """Compress into a copy of ``raw_cache`` (storage dtype kept).  Returns
+    (new raw cache, written mask, fp64 values of the written rows)."""
+    N_cap = raw_cache.shape[1]
+    vals, written = compress(kv_state, score_state, gamma, pos0, ratio, overlap, N_cap, rope_dim, eps=eps,
+                             rope_base=rope_base)
+    new = np.array(raw_cache, copy=True)
+    new[written] = _store_like(raw_cache, vals[written])
+    return new, written, vals
+
+
+def pipeline(inp: dict, eps: float = 1e-6, rope_base: float = 10000.0, topk_override=None) -> dict:
+    """One pass of the whole path for a workload dict (see the workloads
+    module): compress -> [index scores -> top-k] -> attention."""
+    sh = inp["shape"]
+    res = {}
+    cmp_new, written, vals = compress_into(inp["cmp_cache"], inp["kv_state"], inp["score_state"], inp["gamma"],
+                                           inp["state_pos0"], sh.ratio, sh.overlap, sh.rope, eps, rope_base)
+    res["cmp_cache"], res["written"], res["cmp_vals"] = cmp_new, written, vals
+    topk_idx = None
+    if sh.indexer:
+        idx_new, iw, ivals = compress_into(inp["idx_cache"], inp["idx_kv_state"], inp["idx_score_state"],
+                                           inp["idx_gamma"], inp["state_pos0"], sh.ratio, True, sh.idx_rope, eps,
+                                           rope_base)
+        res["idx_cache"], res["idx_written"], res["idx_vals"] = idx_new, iw, ivals
+        scores, nvis = index_scores(inp["q_idx"], inp["w"], idx_new, inp["q_pos"], sh.ratio)
+        topk_idx, kth = topk(scores, nvis, sh.k)
+        res["scores"], res["nvis"], res["topk_idx"], res["kth"] = scores, nvis, topk_idx, kth
+        if topk_override is not None:
+            topk_idx = topk_override
+    out, lse, ncand = attn(inp["q"], cmp_new, inp["win_kv"], inp["sink"], inp["q_pos"], topk_idx=topk_idx,
+                           ratio=sh.ratio, win_pos0=inp.get("win_pos0"), window=sh.window, rope_dim=sh.rope,
+                           rope_base=rope_base)
+    res["out"], res["lse"], res["ncand"] = out, lse, ncand
+    return res

@@ -1,0 +1,422 @@
+"""Pins of the CPU oracle against values the pages print, closed forms,
+invariants, library routines and brute force (no GPU needed).
+
+Sources: "DeepSeek-V4-Pro 架构：一个 token 的旅程" (hs-black.github.io) — sections on
+the shared candidate set and sink, inverse RoPE, per-channel pooling, the
+one-channel worked value, visibility, the indexer and the cost ledger; and
+"图解DeepSeek V4：详细计算流程解析" (jsqmd.com) — sections 2, 2.1 (rolling state),
+2.2, 2.3 and 3.1.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _gold(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return json.load(f)
+
+
+# --------------------------------------------------------------------------- pooling
+def test_pool_worked_value(orc):
+    g = _gold("pool_worked_value.json")
+    r, d = g["ratio"], 1
+    kv = np.zeros((r, 2 * d))
+    sc = np.zeros((r, 2 * d))
+    kv[:, d] = g["own_values"]
+    sc[:, d] = g["own_scores"]
+    kv[:, 0] = 100.0   # first-half channels feed the next entry only
+    sc[:, 0] = 50.0
+    pooled = orc.pool(kv, sc, d, r, True, 0, 0)
+    assert pooled[0] == pytest.approx(g["expected_pooled"], abs=1e-12)
+    # the printed value is before normalisation: RMSNorm of one channel maps it to ~1
+    cache, written = orc.compress(kv[None], sc[None], [1.0], [0], r, True, 1, 0)
+    assert written[0, 0]
+    assert cache[0, 0, 0] == pytest.approx(3.6 / math.sqrt(3.6 ** 2 + 1e-6), rel=1e-12)
+
+
+def _rand_state(rng, L, width):
+    return rng.standard_normal((L, width)), rng.standard_normal((L, width))
+
+
+def test_pool_equal_scores_is_mean(orc):
+    rng = np.random.default_rng(1)
+    r, d = 4, 6
+    kv, _ = _rand_state(rng, 3 * r, 2 * d)
+    sc = np.full_like(kv, 0.7)
+    for g in (1, 2):
+        pooled = orc.pool(kv, sc, d, r, True, 0, g)
+        prev = kv[(g - 1) * r:g * r, :d]
+        own = kv[g * r:(g + 1) * r, d:]
+        np.testing.assert_allclose(pooled, np.concatenate([prev, own]).mean(axis=0), rtol=0, atol=1e-13)
+
+
+def test_pool_dominant_score_selects_its_value(orc):
+    rng = np.random.default_rng(2)
+    r, d = 4, 5
+    kv, sc = _rand_state(rng, 2 * r, 2 * d)
+    sc[1, :d] += 1000.0    # slot 1 of entry 1 (previous group, first half)
+    pooled = orc.pool(kv, sc, d, r, True, 0, 1)
+    np.testing.assert_allclose(pooled, kv[1, :d], atol=1e-12)
+    sc2 = sc.copy()
+    sc2[1, :d] -= 1000.0
+    sc2[6, d:] += 1000.0   # own-group token 6 (second half)
+    pooled = orc.pool(kv, sc2, d, r, True, 0, 1)
+    np.testing.assert_allclose(pooled, kv[6, d:], atol=1e-12)
+
+
+def test_pool_first_group_missing_slots(orc):
+    rng = np.random.default_rng(3)
+    r, d = 4, 7
+    kv, sc = _rand_state(rng, 2 * r, 2 * d)
+    pooled = orc.pool(kv, sc, d, r, True, 0, 0)
+    s = sc[:r, d:]
+    wts = np.exp(s - s.max(axis=0)) / np.exp(s - s.max(axis=0)).sum(axis=0)
+    np.testing.assert_allclose(pooled, (wts * kv[:r, d:]).sum(axis=0), atol=1e-13)
+    assert np.all(np.isfinite(pooled))
+    # entry 0 ignores first-half channels of its own tokens; entry 1 reads them
+    kv2 = kv.copy()
+    kv2[:r, :d] += 5.0
+    np.testing.assert_array_equal(orc.pool(kv2, sc, d, r, True, 0, 0), pooled)
+    assert not np.allclose(orc.pool(kv2, sc, d, r, True, 0, 1), orc.pool(kv, sc, d, r, True, 0, 1))
+
+
+def test_pool_score_shift_invariance(orc):
+    rng = np.random.default_rng(4)
+    r, d = 4, 8
+    kv, sc = _rand_state(rng, 3 * r, 2 * d)
+    shift = rng.standard_normal(d) * 10
+    sc2 = sc.copy()
+    sc2[:, :d] += shift
+    sc2[:, d:] += shift
+    for g in (0, 1, 2):
+        np.testing.assert_allclose(orc.pool(kv, sc2, d, r, True, 0, g), orc.pool(kv, sc, d, r, True, 0, g),
+                                   atol=1e-12)
+
+
+def test_c128a_groups_do_not_overlap(orc):
+    rng = np.random.default_rng(5)
+    r, d = 16, 6
+    kv, sc = _rand_state(rng, 3 * r, d)
+    base = orc.pool(kv, sc, d, r, False, 0, 1)
+    kv2, sc2 = kv.copy(), sc.copy()
+    kv2[:r] += 3.0
+    sc2[2 * r:] -= 2.0
+    np.testing.assert_array_equal(orc.pool(kv2, sc2, d, r, False, 0, 1), base)
+    eq = np.zeros_like(sc)
+    np.testing.assert_allclose(orc.pool(kv, eq, d, r, False, 0, 1), kv[r:2 * r].mean(axis=0), atol=1e-13)
+
+
+# --------------------------------------------------------------------------- compressor
+def test_rolling_state_equals_parallel_form_bitexact(orc):
+    rng = np.random.default_rng(6)
+    B, L, d, r, rope = 2, 64, 16, 4, 8
+    kv = rng.standard_normal((B, L, 2 * d)).astype(np.float32)
+    sc = rng.standard_normal((B, L, 2 * d)).astype(np.float32)
+    gamma = 1 + 0.1 * rng.standard_normal(d)
+    par, written = orc.compress(kv, sc, gamma, [0, 0], r, True, L // r, rope)
+    assert written.all()
+    roll = orc.compress_rolling(kv, sc, gamma, r, L // r, rope)
+    np.testing.assert_array_equal(par, roll)
+
+
+@pytest.mark.parametrize("overlap,expect", [(True, {3, 4}), (False, {2, 3, 4})])
+def test_compress_writes_only_complete_groups(orc, overlap, expect):
+    rng = np.random.default_rng(7)
+    r, d, L = 4, 4, 13       # tokens 8..20
+    m = 2 if overlap else 1
+    kv = rng.standard_normal((1, L, m * d))
+    sc = rng.standard_normal((1, L, m * d))
+    _, written = orc.compress(kv, sc, np.ones(d), [8], r, overlap, 8, 0)
+    assert set(np.nonzero(written[0])[0].tolist()) == expect
+
+
+def test_decode_step_writes_the_completed_entry(orc):
+    rng = np.random.default_rng(8)
+    r, d = 4, 4
+    for t in (4 * 9 + 3, 4 * 9 + 2):
+        kv = rng.standard_normal((1, 8, 2 * d))
+        sc = rng.standard_normal((1, 8, 2 * d))
+        _, written = orc.compress(kv, sc, np.ones(d), [t - 7], r, True, 16, 0)
+        got = set(np.nonzero(written[0])[0].tolist())
+        # (t+1) % ratio == 0  =>  cache[t // ratio] is written, else nothing new is complete
+        assert got == ({t // r} if (t + 1) % r == 0 else set())
+
+
+def test_compressed_rows_unit_rms_and_entry_rotation(orc):
+    rng = np.random.default_rng(9)
+    r, d, L = 4, 2, 12
+    # equal values in every slot => pooled == that value; then RMSNorm; then RoPE at g*r
+    a, b = 0.3, -1.1
+    kv = np.zeros((1, L, 2 * d))
+    kv[..., 0::2] = a
+    kv[..., 1::2] = b
+    sc = rng.standard_normal((1, L, 2 * d))
+    cache, written = orc.compress(kv, sc, np.ones(d), [0], r, True, L // r, d)
+    rms = math.sqrt((a * a + b * b) / 2 + 1e-6)
+    for g in range(L // r):
+        th = g * r            # pair 0 rotates by exactly its position
+        x, y = a / rms, b / rms
+        np.testing.assert_allclose(cache[0, g], [x * math.cos(th) - y * math.sin(th),
+                                                 x * math.sin(th) + y * math.cos(th)], atol=1e-12)
+        assert math.sqrt((cache[0, g] ** 2).mean()) == pytest.approx(1.0, abs=1e-5)
+
+
+# --------------------------------------------------------------------------- RoPE
+def test_rope_closed_forms(orc):
+    for p in (0.0, 1.0, 7.0, 32767.0, 1048575.0):
+        e = np.array([1.0, 0.0])
+        np.testing.assert_allclose(orc.rope(e, p), [math.cos(p), math.sin(p)], atol=1e-12)
+        e4 = np.array([0.0, 0.0, 1.0, 0.0])    # pair 1 of a 4-dim tail: theta = p * 10000^(-1/2)
+        np.testing.assert_allclose(orc.rope(e4, p), [0, 0, math.cos(p / 100.0), math.sin(p / 100.0)], atol=1e-12)
+
+
+def test_rope_norm_inverse_and_relative_position(orc):
+    rng = np.random.default_rng(10)
+    x, y = rng.standard_normal(64), rng.standard_normal(64)
+    for p in (3.0, 4096.0, 1048575.0):
+        rx = orc.rope(x, p)
+        assert np.linalg.norm(rx) == pytest.approx(np.linalg.norm(x), rel=1e-13)
+        np.testing.assert_allclose(orc.rope(rx, p, inverse=True), x, atol=1e-9)
+    d1 = np.dot(orc.rope(x, 100.0), orc.rope(y, 37.0))
+    d2 = np.dot(orc.rope(x, 100.0 + 5000.0), orc.rope(y, 37.0 + 5000.0))
+    assert d1 == pytest.approx(d2, abs=1e-9)
+
+
+# --------------------------------------------------------------------------- visibility + indexer
+def test_visibility_at_group_boundaries(orc):
+    rng = np.random.default_rng(11)
+    r, N, Hi, di = 4, 8, 2, 8
+    q_idx = rng.standard_normal((1, 32, Hi, di))
+    w = rng.standard_normal((1, 32, Hi))
+    cache = rng.standard_normal((1, N, di))
+    scores, nvis = orc.index_scores(q_idx, w, cache, [0], r)
+    for t in range(32):
+        assert nvis[0, t] == (t + 1) // r
+        for g in range(N):
+            # entry g is visible to t iff t >= g*r + r - 1
+            assert np.isfinite(scores[0, t, g]) == (t >= g * r + r - 1)
+
+
+def test_index_single_head_unit_weight_is_relu_dot(orc):
+    rng = np.random.default_rng(12)
+    q = rng.standard_normal((1, 1, 1, 16))
+    cache = rng.standard_normal((1, 40, 16))
+    s, _ = orc.index_scores(q, np.ones((1, 1, 1)), cache, [200], 4)
+    np.testing.assert_allclose(s[0, 0], np.maximum(cache[0] @ q[0, 0, 0], 0.0), atol=1e-12)
+
+
+def test_index_score_linearity_and_relu_identity(orc):
+    rng = np.random.default_rng(13)
+    B, S, Hi, di, N = 2, 3, 4, 8, 30
+    q = rng.standard_normal((B, S, Hi, di))
+    cache = rng.standard_normal((B, N, di))
+    w1, w2 = rng.standard_normal((B, S, Hi)), rng.standard_normal((B, S, Hi))
+    qp = [500, 500]
+    s1, _ = orc.index_scores(q, w1, cache, qp, 4)
+    s2, _ = orc.index_scores(q, w2, cache, qp, 4)
+    s12, _ = orc.index_scores(q, w1 + w2, cache, qp, 4)
+    np.testing.assert_allclose(s12, s1 + s2, atol=1e-12)
+    sneg, _ = orc.index_scores(-q, w1, cache, qp, 4)
+    # relu(x) - relu(-x) == x: the difference is the plain weighted dot product
+    lin = np.einsum("bsh,bshn->bsn", w1, np.matmul(q, np.swapaxes(cache, 1, 2)[:, None]))
+    np.testing.assert_allclose(s1 - sneg, lin, atol=1e-12)
+    slin, _ = orc.index_scores(q, w1, cache, qp, 4, relu=False)
+    np.testing.assert_allclose(slin, lin, atol=1e-12)
+
+
+# --------------------------------------------------------------------------- top-k
+def test_topk_matches_stable_argsort(orc):
+    rng = np.random.default_rng(14)
+    B, S, N, k = 2, 5, 200, 17
+    s = np.round(rng.standard_normal((B, S, N)), 1)   # many ties
+    nvis = rng.integers(0, N + 1, size=(B, S)).astype(np.int32)
+    nvis[0, 0], nvis[0, 1] = 0, 5
+    idx, kth = orc.topk(s, nvis, k)
+    for b in range(B):
+        for t in range(S):
+            nv = nvis[b, t]
+            ref = np.argsort(-s[b, t, :nv], kind="stable")[:min(k, nv)]
+            np.testing.assert_array_equal(idx[b, t, :len(ref)], ref)
+            assert np.all(idx[b, t, len(ref):] == -1)
+            if len(ref):
+                assert kth[b, t] == s[b, t, ref[-1]]
+
+
+def test_topk_equal_scores_prefer_lower_index(orc):
+    s = np.zeros((1, 1, 50))
+    idx, _ = orc.topk(s, np.array([[40]], dtype=np.int32), 8)
+    np.testing.assert_array_equal(idx[0, 0], np.arange(8))
+
+
+# --------------------------------------------------------------------------- attention
+def _candidates(win, cmp, b, t, window, W_cap, topk_row=None, nvis=None):
+    """Rows of the candidate set: window positions [max(0,t-window+1), t] of a
+    ring buffer, then the listed compressed entries (or all visible ones)."""
+    rows = [win[b, u % W_cap] for u in range(max(0, t - window + 1), t + 1)]
+    ents = [e for e in topk_row if e >= 0] if topk_row is not None else range(nvis)
+    rows += [cmp[b, e] for e in ents]
+    return np.stack(rows)
+
+
+def test_attention_without_sink_is_masked_softmax_attention(orc):
+    rng = np.random.default_rng(15)
+    B, S, H, D, N, W_cap, window, k = 2, 3, 4, 16, 20, 8, 5, 6
+    q = rng.standard_normal((B, S, H, D))
+    cmp = rng.standard_normal((B, N, D))
+    win = rng.standard_normal((B, W_cap, D))
+    qp = [40, 61]
+    topk = rng.integers(-1, 10, size=(B, S, k)).astype(np.int32)
+    scale = 0.37
+    out, _, _ = orc.attn(q, cmp, win, np.full(H, -np.inf), qp, topk_idx=topk, window=window, rope_dim=0,
+                         scale=scale)
+    for b in range(B):
+        for s in range(S):
+            t = qp[b] + s
+            rows = torch.from_numpy(_candidates(win, cmp, b, t, window, W_cap, topk_row=topk[b, s]))
+            qq = torch.from_numpy(q[b, s])[:, None, :]               # [H, 1, D]
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                qq, rows[None].expand(H, -1, -1), rows[None].expand(H, -1, -1), scale=scale)
+            np.testing.assert_allclose(out[b, s], ref[:, 0].numpy(), atol=1e-12)
+
+
+def test_attention_identical_rows_closed_form_and_sink_mass(orc):
+    rng = np.random.default_rng(16)
+    H, D, N, W_cap, window = 3, 8, 12, 16, 16
+    c = rng.standard_normal(D)
+    q = rng.standard_normal((1, 1, H, D))
+    sink = rng.standard_normal(H)
+    cmp = np.broadcast_to(c, (1, N, D)).copy()
+    win = np.broadcast_to(c, (1, W_cap, D)).copy()
+    t = 4 * N - 1
+    scale = 1 / math.sqrt(D)
+    out, lse, ncand = orc.attn(q, cmp, win, sink, [t], topk_idx=None, ratio=4, window=window, rope_dim=0,
+                               scale=scale)
+    n = window + N
+    assert ncand[0, 0] == n
+    for h in range(H):
+        logit = scale * np.dot(q[0, 0, h], c)
+        mass = n / (n + math.exp(sink[h] - logit))      # total attention weight on values
+        assert mass < 1.0
+        np.testing.assert_allclose(out[0, 0, h], c * mass, atol=1e-12)
+        assert lse[0, 0, h] == pytest.approx(math.log(n * math.exp(logit) + math.exp(sink[h])), abs=1e-12)
+
+
+def test_attention_output_is_derotated_at_query_position(orc):
+    D, t = 4, 1234
+    c = np.array([1.0, 0.0, 0.0, 0.0])
+    cmp = np.broadcast_to(c, (1, 400, D)).copy()
+    win = np.broadcast_to(c, (1, 8, D)).copy()
+    q = np.zeros((1, 1, 1, D))
+    out, _, ncand = orc.attn(q, cmp, win, [-np.inf], [t], topk_idx=None, ratio=4, window=8, rope_dim=D)
+    # all weight on identical rows => o == c; pair 0 is then rotated by -t
+    np.testing.assert_allclose(out[0, 0, 0], [math.cos(t), -math.sin(t), 0, 0], atol=1e-9)
+
+
+def test_csa_with_all_visible_entries_equals_dense(orc):
+    rng = np.random.default_rng(17)
+    B, H, D, N, W_cap, window = 2, 2, 16, 40, 8, 8
+    qp = [71, 130]
+    q = rng.standard_normal((B, 1, H, D))
+    cmp = rng.standard_normal((B, N, D))
+    win = rng.standard_normal((B, W_cap, D))
+    sink = rng.standard_normal(H)
+    k = 64
+    topk = np.full((B, 1, k), -1, dtype=np.int32)
+    for b in range(B):
+        nv = (qp[b] + 1) // 4
+        topk[b, 0, :nv] = rng.permutation(nv)
+    sp, slse, _ = orc.attn(q, cmp, win, sink, qp, topk_idx=topk, window=window, rope_dim=8)
+    de, dlse, _ = orc.attn(q, cmp, win, sink, qp, topk_idx=None, ratio=4, window=window, rope_dim=8)
+    np.testing.assert_allclose(sp, de, atol=1e-12)
+    np.testing.assert_allclose(slse, dlse, atol=1e-12)
+
+
+def test_ledger_read_counts(orc):
+    g = _gold("attention_ledger.json")
+    Hh, Dd = g["heads"], g["head_dim"]
+    c = g["csa_32k"]
+    t = c["position"]
+    N = (t + 1) // c["ratio"]
+    q = np.zeros((1, 1, 1, 2))
+    cmp = np.zeros((1, N, 2))
+    win = np.zeros((1, c["window"], 2))
+    topk = np.arange(c["topk"], dtype=np.int32)[None, None]
+    _, _, nc = orc.attn(q, cmp, win, [0.0], [t], topk_idx=topk, window=c["window"], rope_dim=0)
+    assert round(4 * Hh * int(nc[0, 0]) * Dd / 1e6) == c["approx_mflop"]
+    h = g["hca_32k"]
+    cmp = np.zeros((1, (t + 1) // h["ratio"], 2))
+    _, _, nc = orc.attn(q, cmp, win, [0.0], [t], topk_idx=None, ratio=h["ratio"], window=h["window"], rope_dim=0)
+    assert round(4 * Hh * int(nc[0, 0]) * Dd / 1e6) == h["approx_mflop"]
+
+
+# --------------------------------------------------------------------------- whole path
+def _tiny_f64():
+    from compressed_sparse_attention_c4a_amd import workloads as W
+    inp = W.tiny_fp32()
+    inp["cmp_cache"] = inp["cmp_cache"].astype(np.float64)
+    inp["idx_cache"] = inp["idx_cache"].astype(np.float64)
+    return inp
+
+
+def _dense_args(inp):
+    sh = inp["shape"]
+    return {"kv_state": inp["kv_state"], "score_state": inp["score_state"], "ratio": sh.ratio,
+            "overlap": sh.overlap, "rope_dim": sh.rope, "gamma": inp["gamma"],
+            "idx_kv_state": inp["idx_kv_state"], "idx_score_state": inp["idx_score_state"],
+            "idx_gamma": inp["idx_gamma"], "idx_rope_dim": sh.idx_rope, "q_idx": inp["q_idx"], "w": inp["w"],
+            "k": sh.k, "q": inp["q"], "win_kv": inp["win_kv"], "window": sh.window, "sink": inp["sink"]}
+
+
+def test_dense_mask_formulation_agrees_with_gather_oracle(orc):
+    inp = _tiny_f64()
+    r = orc.pipeline(inp)
+    R = orc.dense_pipeline(_dense_args(inp))
+    np.testing.assert_allclose(R["cache"], r["cmp_vals"], atol=1e-12)
+    np.testing.assert_allclose(R["icache"], r["idx_vals"], atol=1e-12)
+    np.testing.assert_allclose(R["out"], r["out"], atol=1e-12)
+    np.testing.assert_allclose(R["lse"], r["lse"], atol=1e-12)
+    sel_c = np.zeros_like(R["sel"])
+    for t in range(R["sel"].shape[1]):
+        ids = r["topk_idx"][0, t]
+        sel_c[0, t, ids[ids >= 0]] = True
+    np.testing.assert_array_equal(sel_c, R["sel"])
+
+
+def test_hca_dense_formulation_agrees(orc):
+    rng = np.random.default_rng(18)
+    T, d, r, H = 64, 16, 8, 2
+    inp = {"kv_state": rng.standard_normal((1, T, d)), "score_state": rng.standard_normal((1, T, d)),
+           "ratio": r, "overlap": False, "rope_dim": 4, "gamma": 1 + 0.1 * rng.standard_normal(d), "hca": True,
+           "q": rng.standard_normal((1, T, H, d)), "win_kv": rng.standard_normal((1, T, d)), "window": 8,
+           "sink": rng.standard_normal(H)}
+    R = orc.dense_pipeline(inp)
+    cache, written = orc.compress(inp["kv_state"], inp["score_state"], inp["gamma"], [0], r, False, T // r, 4)
+    np.testing.assert_allclose(cache, R["cache"], atol=1e-12)
+    out, lse, _ = orc.attn(inp["q"], cache, inp["win_kv"], inp["sink"], [0], topk_idx=None, ratio=r,
+                           win_pos0=[0], window=8, rope_dim=4)
+    np.testing.assert_allclose(out, R["out"], atol=1e-12)
+
+
+def test_queries_never_see_the_future(orc):
+    inp = _tiny_f64()
+    base = orc.pipeline(inp)
+    t0 = 37
+    pert = dict(inp)
+    rng = np.random.default_rng(19)
+    for key in ("kv_state", "score_state", "idx_kv_state", "idx_score_state", "win_kv", "q", "q_idx"):
+        a = np.array(inp[key], copy=True)
+        a[:, t0 + 1:] = rng.standard_normal(a[:, t0 + 1:].shape)
+        pert[key] = a
+    w = np.array(inp["w"], copy=True)
+    w[:, t0 + 1:] = rng.standard_normal(w[:, t0 + 1:].shape)
+    pert["w"] = w
+    got = orc.pipeline(pert)
+    np.testing.assert_array_equal(got["out"][:, :t0 + 1], base["out"][:, :t0 + 1])
+    np.testing.assert_array_equal(got["topk_idx"][:, :t0 + 1], base["topk_idx"][:, :t0 + 1])

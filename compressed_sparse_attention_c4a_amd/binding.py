@@ -1,0 +1,195 @@
+"""ctypes binding of libcsa.so: the same entry points as include/csa.h, taking
+torch tensors.  It only checks devices, dtypes and contiguity, derives sizes
+from tensor shapes and passes raw device pointers; every computation runs in
+the HIP kernels.  There is no fallback: if libcsa.so is missing or a call
+fails, a RuntimeError is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libcsa.so")
+HEADER = os.path.join(os.path.dirname(_PKG), "include", "csa.h")
+
+CSA_F32, CSA_BF16 = 0, 1
+CSA_INDEX_NO_RELU = 1
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libcsa.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m compressed_sparse_attention_c4a_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, f32, u32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_uint, ctypes.c_size_t
+    sigs = {
+        "csa_version": ([], i32),
+        "csa_error_string": ([i32], ctypes.c_char_p),
+        "csa_last_error": ([], ctypes.c_char_p),
+        "csa_compress": ([vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, f32, i32, vp], i32),
+        "csa_index_scores": ([vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, u32, i32, vp], i32),
+        "csa_topk_workspace_size": ([i32, i32, i32, i32], sz),
+        "csa_topk": ([vp, vp, vp, vp, vp, sz, i32, i32, i32, i32, i32, vp], i32),
+        "csa_index_topk_workspace_size": ([i32, i32, i32, i32], sz),
+        "csa_index_topk": ([vp, vp, vp, vp, vp, vp, vp, sz, i32, i32, i32, i32, i32, i32, i32, u32, i32, vp], i32),
+        "csa_attn_workspace_size": ([i32, i32, i32, i32, i32], sz),
+        "csa_sparse_attn": ([vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i32, i32, i32, i32, i32, i32, i32, i32, i32,
+                             f32, f32, i32, vp], i32),
+        "hca_attn": ([vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i32, i32, i32, i32, i32, i32, i32, i32, i32, f32, f32,
+                      i32, vp], i32),
+    }
+    for name, (args, res) in sigs.items():
+        fn = getattr(L, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = L
+    return L
+
+
+def declared_functions() -> list:
+    """Names of the functions include/csa.h declares."""
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\**\s*((?:csa|hca)_\w+)\s*\(", text, flags=re.M)))
+
+
+# ----------------------------------------------------------------------------- marshalling helpers
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return CSA_F32
+    if t.dtype == torch.bfloat16:
+        return CSA_BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _ptr(t: Optional[torch.Tensor], dtype=None, name="tensor"):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _check(rc: int, name: str):
+    if rc != 0:
+        L = load()
+        raise RuntimeError(f"{name} failed ({L.csa_error_string(rc).decode()}): {L.csa_last_error().decode()}")
+
+
+# ----------------------------------------------------------------------------- entry points
+def csa_version() -> int:
+    return load().csa_version()
+
+
+def csa_compress(kv_state, score_state, gamma, cache, pos0, *, ratio: int, overlap: bool, rope_dim: int,
+                 eps: float = 1e-6, rope_base: float = 10000.0, stream=None):
+    B, L, md = kv_state.shape
+    d = cache.shape[-1]
+    if md != (2 if overlap else 1) * d or score_state.shape != kv_state.shape:
+        raise ValueError("state width must be (2 if overlap else 1) * d and kv/score shapes must match")
+    dt = _dtype_code(kv_state)
+    rc = load().csa_compress(_ptr(kv_state, kv_state.dtype, "kv_state"), _ptr(score_state, kv_state.dtype, "score_state"),
+                             _ptr(gamma, torch.float32, "gamma"), _ptr(cache, kv_state.dtype, "cache"),
+                             _ptr(pos0, torch.int32, "pos0"), B, L, d, rope_dim, ratio, int(overlap), cache.shape[1],
+                             eps, rope_base, dt, _stream(stream))
+    _check(rc, "csa_compress")
+
+
+def csa_index_scores(q_idx, w, idx_cache, q_pos, scores, *, ratio: int, relu: bool = True, stream=None):
+    B, S, Hi, di = q_idx.shape
+    N_cap = idx_cache.shape[1]
+    rc = load().csa_index_scores(_ptr(q_idx, q_idx.dtype, "q_idx"), _ptr(w, torch.float32, "w"),
+                                 _ptr(idx_cache, q_idx.dtype, "idx_cache"), _ptr(q_pos, torch.int32, "q_pos"),
+                                 _ptr(scores, torch.float32, "scores"), B, S, Hi, di, N_cap, ratio,
+                                 0 if relu else CSA_INDEX_NO_RELU, _dtype_code(q_idx), _stream(stream))
+    _check(rc, "csa_index_scores")
+
+
+def csa_topk_workspace_size(B: int, S: int, N_cap: int, k: int) -> int:
+    return load().csa_topk_workspace_size(B, S, N_cap, k)
+
+
+def csa_topk(scores, q_pos, topk_idx, topk_score=None, *, ratio: int, workspace=None, stream=None):
+    B, S, N_cap = scores.shape
+    k = topk_idx.shape[-1]
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = load().csa_topk(_ptr(scores, torch.float32, "scores"), _ptr(q_pos, torch.int32, "q_pos"),
+                         _ptr(topk_idx, torch.int32, "topk_idx"), _ptr(topk_score, torch.float32, "topk_score"),
+                         _ptr(workspace, None, "workspace"), ws_bytes, B, S, N_cap, k, ratio, _stream(stream))
+    _check(rc, "csa_topk")
+
+
+def csa_index_topk_workspace_size(B: int, S: int, N_cap: int, k: int) -> int:
+    return load().csa_index_topk_workspace_size(B, S, N_cap, k)
+
+
+def csa_index_topk(q_idx, w, idx_cache, q_pos, topk_idx, topk_score=None, *, ratio: int, workspace,
+                   relu: bool = True, stream=None):
+    B, S, Hi, di = q_idx.shape
+    N_cap = idx_cache.shape[1]
+    k = topk_idx.shape[-1]
+    ws_bytes = workspace.numel() * workspace.element_size()
+    rc = load().csa_index_topk(_ptr(q_idx, q_idx.dtype, "q_idx"), _ptr(w, torch.float32, "w"),
+                               _ptr(idx_cache, q_idx.dtype, "idx_cache"), _ptr(q_pos, torch.int32, "q_pos"),
+                               _ptr(topk_idx, torch.int32, "topk_idx"), _ptr(topk_score, torch.float32, "topk_score"),
+                               _ptr(workspace, None, "workspace"), ws_bytes, B, S, Hi, di, N_cap, k, ratio,
+                               0 if relu else CSA_INDEX_NO_RELU, _dtype_code(q_idx), _stream(stream))
+    _check(rc, "csa_index_topk")
+
+
+def csa_attn_workspace_size(B: int, S: int, H: int, D: int, n_cand: int) -> int:
+    return load().csa_attn_workspace_size(B, S, H, D, n_cand)
+
+
+def csa_sparse_attn(q, cmp_cache, topk_idx, win_kv, win_pos0, sink, q_pos, out, lse=None, *, rope_dim: int,
+                    window: int, softmax_scale: Optional[float] = None, rope_base: float = 10000.0, workspace=None,
+                    stream=None):
+    B, S, H, D = q.shape
+    N_cap = cmp_cache.shape[1]
+    k = topk_idx.shape[-1]
+    W_cap = win_kv.shape[1]
+    scale = softmax_scale if softmax_scale is not None else D ** -0.5
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = load().csa_sparse_attn(_ptr(q, q.dtype, "q"), _ptr(cmp_cache, q.dtype, "cmp_cache"),
+                                _ptr(topk_idx, torch.int32, "topk_idx"), _ptr(win_kv, q.dtype, "win_kv"),
+                                _ptr(win_pos0, torch.int32, "win_pos0"), _ptr(sink, torch.float32, "sink"),
+                                _ptr(q_pos, torch.int32, "q_pos"), _ptr(out, q.dtype, "out"),
+                                _ptr(lse, torch.float32, "lse"), _ptr(workspace, None, "workspace"), ws_bytes, B, S, H,
+                                D, rope_dim, N_cap, k, W_cap, window, scale, rope_base, _dtype_code(q),
+                                _stream(stream))
+    _check(rc, "csa_sparse_attn")
+
+
+def hca_attn(q, cmp_cache, win_kv, win_pos0, sink, q_pos, out, lse=None, *, ratio: int, rope_dim: int, window: int,
+             softmax_scale: Optional[float] = None, rope_base: float = 10000.0, workspace=None, stream=None):
+    B, S, H, D = q.shape
+    N_cap = cmp_cache.shape[1]
+    W_cap = win_kv.shape[1]
+    scale = softmax_scale if softmax_scale is not None else D ** -0.5
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = load().hca_attn(_ptr(q, q.dtype, "q"), _ptr(cmp_cache, q.dtype, "cmp_cache"), _ptr(win_kv, q.dtype, "win_kv"),
+                         _ptr(win_pos0, torch.int32, "win_pos0"), _ptr(sink, torch.float32, "sink"),
+                         _ptr(q_pos, torch.int32, "q_pos"), _ptr(out, q.dtype, "out"), _ptr(lse, torch.float32, "lse"),
+                         _ptr(workspace, None, "workspace"), ws_bytes, B, S, H, D, rope_dim, N_cap, ratio, W_cap,
+                         window, scale, rope_base, _dtype_code(q), _stream(stream))
+    _check(rc, "hca_attn")

@@ -1,0 +1,102 @@
+// common.hpp -- device helpers shared by the gfx950 kernels of libcsa.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/csa.h"
+
+namespace csa {
+
+// bf16 is stored as its raw 16-bit pattern (the high half of an IEEE binary32).
+struct bf16 {
+  uint16_t x;
+};
+
+__device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// fp32 -> bf16, round to nearest even (inputs here are finite).
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+template <typename T>
+struct Elt;
+template <>
+struct Elt<float> {
+  static __device__ __forceinline__ float ld(const float* p, size_t i) { return p[i]; }
+  static __device__ __forceinline__ void st(float* p, size_t i, float v) { p[i] = v; }
+};
+template <>
+struct Elt<bf16> {
+  static __device__ __forceinline__ float ld(const bf16* p, size_t i) { return bf2f(p[i].x); }
+  static __device__ __forceinline__ void st(bf16* p, size_t i, float v) { p[i].x = f2bf(v); }
+};
+
+// floor(a / b) for b > 0
+__device__ __forceinline__ long floor_div(long a, long b) { return a >= 0 ? a / b : -((-a + b - 1) / b); }
+
+// Number of compressed entries visible to query position t: (t+1)/ratio, clamped to [0, N_cap].
+__device__ __forceinline__ long visible_entries(long t, int ratio, int N_cap) {
+  long nv = floor_div(t + 1, ratio);
+  if (nv < 0) nv = 0;
+  if (nv > N_cap) nv = N_cap;
+  return nv;
+}
+
+// RoPE rotation of interleaved pair i of a rope_dim-wide tail at position pos:
+// theta = pos * base^(-2i/rope_dim).  Angles are formed and reduced in double so
+// that positions up to 2^20 keep full fp32 accuracy in cos/sin.
+__device__ __forceinline__ void rope_cos_sin(double pos, int i, int rope_dim, float base, float* c, float* s) {
+  double inv_freq = pow((double)base, -2.0 * (double)i / (double)rope_dim);
+  double th = pos * inv_freq;
+  double sn, cs;
+  sincos(th, &sn, &cs);
+  *c = (float)cs;
+  *s = (float)sn;
+}
+
+// Workgroups are dispatched round-robin over the 8 XCDs (block L -> XCD L % 8),
+// each with its own L2.  This bijection on [0, total) gives every XCD one
+// contiguous range of work items, so items that share data (e.g. the head
+// groups of one query) run under the same L2.
+__device__ __forceinline__ int xcd_remap(int L, int total) {
+  const int per = total / 8, rem = total % 8;
+  const int x = L % 8, j = L / 8;
+  return x * per + (x < rem ? x : rem) + j;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+}  // namespace csa
+
+// Host-side launch helpers implemented per kernel file; called from abi.cpp.
+namespace csa_host {
+hipError_t launch_compress(const void* kv, const void* sc, const float* gamma, void* cache, const int32_t* pos0, int B,
+                           int L, int d, int rope_dim, int ratio, int overlap, int N_cap, float eps, float base,
+                           int dtype, hipStream_t st);
+hipError_t launch_index_scores(const void* q, const float* w, const void* K, const int32_t* q_pos, float* scores,
+                               int B, int S, int Hi, int di, int N_cap, int ratio, unsigned flags, int dtype,
+                               hipStream_t st);
+size_t topk_workspace_size(int B, int S, int N_cap, int k);
+hipError_t launch_topk(const float* scores, const int32_t* q_pos, int32_t* idx, float* val, void* ws, int B, int S,
+                       int N_cap, int k, int ratio, hipStream_t st);
+size_t attn_workspace_size(int B, int S, int H, int D, int n_cand);
+hipError_t launch_attn(const void* q, const void* cmp, const int32_t* topk_idx, int k, int dense, int ratio,
+                       const void* win,
+                       const int32_t* win_pos0, const float* sink, const int32_t* q_pos, void* out, float* lse,
+                       void* ws, int B, int S, int H, int D, int rope_dim, int N_cap, int W_cap, int window,
+                       float scale, float base, int dtype, hipStream_t st);
+}  // namespace csa_host

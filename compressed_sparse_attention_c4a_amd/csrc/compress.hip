@@ -1,0 +1,115 @@
+// compress.hip -- token-level compressors C4A (ratio 4, overlapping 2*ratio
+// state) and C128A (ratio 128, non-overlapping).
+//
+// "DeepSeek-V4-Pro 架构：一个 token 的旅程", sections "压缩是逐通道的 learned pooling"
+// (softmax over the token axis per channel, then RMSNorm, then RoPE on the
+// tail dims), "一个通道，逐项算出压缩结果" (entry 0 has no previous group: those
+// slots weigh 0) and "压缩条目必须等整组完成后才可见" (an entry exists once its
+// group is complete).  "图解DeepSeek V4" 2.1: a C4A entry pools the previous
+// group's first-half channels together with its own group's second-half
+// channels; 3.1: C128A pools its own 128 tokens only.
+//
+// One workgroup per (sequence, candidate group); thread p owns the channel
+// pair (2p, 2p+1), which is also a RoPE pair.  Slots are folded with an online
+// softmax in fp32.  Memory-bound and tiny next to the indexer and attention.
+#include "common.hpp"
+
+namespace csa {
+
+template <typename T>
+__global__ __launch_bounds__(256) void compress_kernel(const T* __restrict__ kv, const T* __restrict__ sc,
+                                                       const float* __restrict__ gamma, T* __restrict__ cache,
+                                                       const int32_t* __restrict__ pos0, int L, int d, int rope_dim,
+                                                       int ratio, int overlap, int N_cap, float eps, float base) {
+  const int b = blockIdx.y;
+  const long p0 = pos0[b];
+  const long g = floor_div(p0, ratio) + blockIdx.x;
+  const long first = g * ratio, last = first + ratio - 1;
+  // The whole block takes the same exit: every condition depends on (b, g) only.
+  if (g < 0 || g >= N_cap || first < p0 || last > p0 + L - 1) return;
+  if (overlap && g > 0 && first - ratio < p0) return;
+
+  const int m = overlap ? 2 : 1;
+  const size_t row_w = (size_t)m * d;
+  const T* kvb = kv + (size_t)b * L * row_w;
+  const T* scb = sc + (size_t)b * L * row_w;
+
+  const int p = threadIdx.x;
+  const bool active = 2 * p < d;
+  float y[2] = {0.f, 0.f};
+  if (active) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int c = 2 * p + h;
+      float mx = -INFINITY, den = 0.f, num = 0.f;
+      const int nslot = overlap ? 2 * ratio : ratio;
+      for (int j = 0; j < nslot; ++j) {
+        long tok;
+        int ch;
+        if (overlap && j < ratio) {
+          if (g == 0) continue;  // missing previous group: weight 0
+          tok = first - ratio + j;
+          ch = c;
+        } else {
+          tok = first + (overlap ? j - ratio : j);
+          ch = overlap ? d + c : c;
+        }
+        const size_t off = (size_t)(tok - p0) * row_w + ch;
+        const float s = Elt<T>::ld(scb, off);
+        const float v = Elt<T>::ld(kvb, off);
+        if (s > mx) {
+          const float r = expf(mx - s);
+          den *= r;
+          num *= r;
+          mx = s;
+        }
+        const float e = expf(s - mx);
+        den += e;
+        num += e * v;
+      }
+      y[h] = num / den;
+    }
+  }
+
+  // RMSNorm over the d channels of the entry.
+  __shared__ float part[4];
+  float ss = wave_sum(y[0] * y[0] + y[1] * y[1]);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float tot = part[0] + part[1] + part[2] + part[3];
+  const float inv = 1.0f / sqrtf(tot / (float)d + eps);
+  if (!active) return;
+  float a = y[0] * inv * gamma[2 * p], bb = y[1] * inv * gamma[2 * p + 1];
+  const int tail0 = d - rope_dim;
+  if (2 * p >= tail0) {
+    float cs, sn;
+    rope_cos_sin((double)first, p - tail0 / 2, rope_dim, base, &cs, &sn);
+    const float ra = a * cs - bb * sn, rb = a * sn + bb * cs;
+    a = ra;
+    bb = rb;
+  }
+  T* dst = cache + ((size_t)b * N_cap + g) * d;
+  Elt<T>::st(dst, 2 * p, a);
+  Elt<T>::st(dst, 2 * p + 1, bb);
+}
+
+}  // namespace csa
+
+namespace csa_host {
+using namespace csa;
+
+hipError_t launch_compress(const void* kv, const void* sc, const float* gamma, void* cache, const int32_t* pos0, int B,
+                           int L, int d, int rope_dim, int ratio, int overlap, int N_cap, float eps, float base,
+                           int dtype, hipStream_t st) {
+  // Groups that can intersect [pos0, pos0 + L): at most ceil(L / ratio) + 1.
+  dim3 grid((unsigned)((L + ratio - 1) / ratio + 1), (unsigned)B);
+  if (dtype == CSA_F32)
+    hipLaunchKernelGGL(compress_kernel<float>, grid, dim3(256), 0, st, (const float*)kv, (const float*)sc, gamma,
+                       (float*)cache, pos0, L, d, rope_dim, ratio, overlap, N_cap, eps, base);
+  else
+    hipLaunchKernelGGL(compress_kernel<bf16>, grid, dim3(256), 0, st, (const bf16*)kv, (const bf16*)sc, gamma,
+                       (bf16*)cache, pos0, L, d, rope_dim, ratio, overlap, N_cap, eps, base);
+  return hipGetLastError();
+}
+
+}  // namespace csa_host

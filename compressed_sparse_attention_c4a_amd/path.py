@@ -1,0 +1,69 @@
+"""One pass of the compressed attention hot path on device tensors:
+
+    csa_compress (main KV) -> csa_compress (index keys) -> csa_index_topk
+      -> csa_sparse_attn                                  (CSA layers)
+    csa_compress (C128A) -> hca_attn                      (HCA layers)
+
+Every step is a libcsa call; this module only moves the generated inputs to
+the device and allocates outputs and workspaces.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import binding as K
+from .workloads import Shape
+
+
+def _dev(a: np.ndarray, device) -> torch.Tensor:
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a).to(device).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+def to_device(inp: dict, device="cuda") -> dict:
+    """Copy a generated workload (numpy) to the device."""
+    out = {"shape": inp["shape"]}
+    for key, val in inp.items():
+        if key != "shape":
+            out[key] = None if val is None else _dev(val, device)
+    return out
+
+
+class Step:
+    """Outputs and workspaces of one pass, allocated once and reused."""
+
+    def __init__(self, dev: dict):
+        sh: Shape = dev["shape"]
+        self.sh = sh
+        q = dev["q"]
+        device = q.device
+        self.out = torch.empty_like(q)
+        self.lse = torch.empty((sh.B, sh.S, sh.H), dtype=torch.float32, device=device)
+        if sh.indexer:
+            self.topk_idx = torch.empty((sh.B, sh.S, sh.k), dtype=torch.int32, device=device)
+            ws = K.csa_index_topk_workspace_size(sh.B, sh.S, sh.N_cap, sh.k)
+            self.idx_ws = torch.empty(max(ws, 1), dtype=torch.uint8, device=device)
+            aws = K.csa_attn_workspace_size(sh.B, sh.S, sh.H, sh.D, sh.window + sh.k)
+        else:
+            aws = K.csa_attn_workspace_size(sh.B, sh.S, sh.H, sh.D, sh.window + sh.N_cap)
+        self.attn_ws = torch.empty(max(aws, 1), dtype=torch.uint8, device=device) if aws else None
+
+    def run(self, dev: dict, stream=None):
+        sh = self.sh
+        K.csa_compress(dev["kv_state"], dev["score_state"], dev["gamma"], dev["cmp_cache"], dev["state_pos0"],
+                       ratio=sh.ratio, overlap=sh.overlap, rope_dim=sh.rope, stream=stream)
+        if sh.indexer:
+            K.csa_compress(dev["idx_kv_state"], dev["idx_score_state"], dev["idx_gamma"], dev["idx_cache"],
+                           dev["state_pos0"], ratio=sh.ratio, overlap=True, rope_dim=sh.idx_rope, stream=stream)
+            K.csa_index_topk(dev["q_idx"], dev["w"], dev["idx_cache"], dev["q_pos"], self.topk_idx,
+                             ratio=sh.ratio, workspace=self.idx_ws, stream=stream)
+            K.csa_sparse_attn(dev["q"], dev["cmp_cache"], self.topk_idx, dev["win_kv"], dev.get("win_pos0"),
+                              dev["sink"], dev["q_pos"], self.out, self.lse, rope_dim=sh.rope, window=sh.window,
+                              workspace=self.attn_ws, stream=stream)
+        else:
+            K.hca_attn(dev["q"], dev["cmp_cache"], dev["win_kv"], dev.get("win_pos0"), dev["sink"], dev["q_pos"],
+                       self.out, self.lse, ratio=sh.ratio, rope_dim=sh.rope, window=sh.window,
+                       workspace=self.attn_ws, stream=stream)
+        return self.out

@@ -1,0 +1,175 @@
+/*
+ * csa.h -- C ABI of the MI355X (gfx950) compressed attention library
+ * (libcsa.so): DeepSeek-V4 token-level compressors (C4A, C128A), the
+ * indexer with top-k selection, and multi-query attention over a sliding
+ * window plus compressed entries with a learned sink and inverse RoPE.
+ *
+ * Sources (page titles as published):
+ *   [P1] "DeepSeek-V4-Pro 架构：一个 token 的旅程" (hs-black.github.io)
+ *   [P5] "图解DeepSeek V4：详细计算流程解析" (jsqmd.com)
+ *
+ * Conventions for every entry point
+ *   - Tensor pointers are DEVICE pointers to contiguous row-major arrays owned
+ *     by the caller.  The library never allocates, frees or synchronises; it
+ *     enqueues kernels on `stream` (a hipStream_t; NULL is the null stream)
+ *     and returns.  Kernels may still be running when a call returns.
+ *   - `dtype` is CSA_F32 or CSA_BF16 and applies to q, q_idx, caches, window
+ *     rows, compressor states and attention outputs.  gamma, w, sink and
+ *     scores are always fp32; positions and indices are int32.
+ *   - Positions are per batch row (device int32 arrays of length B), so every
+ *     request may have its own length.  Visibility, windows and RoPE angles
+ *     are derived from them inside the kernels.
+ *   - Arguments are validated on the host before anything is enqueued; on a
+ *     violation the call returns a negative CSA_ERR_* code, enqueues nothing,
+ *     and csa_last_error() (thread-local) describes the problem.  A launch
+ *     failure returns CSA_ERR_HIP.  Values inside device arrays (positions,
+ *     indices) are not visible to the host: kernels skip entries that fall
+ *     outside the buffers instead of reading out of bounds.
+ *   - Every pointer must be 16-byte aligned (CSA_ERR_ALIGN otherwise).
+ *   - Calls are re-entrant: no state is kept between calls.
+ */
+#ifndef CSA_H
+#define CSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* csa_stream_t; /* identical to hipStream_t */
+
+#define CSA_F32 0
+#define CSA_BF16 1
+
+#define CSA_OK 0
+#define CSA_ERR_NULL (-1)        /* a required pointer is NULL */
+#define CSA_ERR_SHAPE (-2)       /* a size is out of range or sizes disagree */
+#define CSA_ERR_DTYPE (-3)       /* dtype is neither CSA_F32 nor CSA_BF16 */
+#define CSA_ERR_UNSUPPORTED (-4) /* no kernel instantiation for this size */
+#define CSA_ERR_ALIGN (-5)       /* a pointer is not 16-byte aligned */
+#define CSA_ERR_WORKSPACE (-6)   /* workspace missing or too small */
+#define CSA_ERR_HIP (-7)         /* the HIP runtime reported a launch error */
+
+/* Flags of csa_index_scores / csa_index_topk. */
+#define CSA_INDEX_NO_RELU 1u /* score = sum_h w_h * (q_h . k), without ReLU */
+
+int csa_version(void);
+const char* csa_error_string(int code);
+const char* csa_last_error(void); /* detail of the calling thread's last error */
+
+/*
+ * csa_compress -- token-level compressor, [P1] "压缩是逐通道的 learned pooling",
+ * "一个通道，逐项算出压缩结果", "压缩条目必须等整组完成后才可见"; [P5] 2.1 (C4A) and
+ * 3.1 (C128A).
+ *
+ * kv_state, score_state: [B, L, m*d], m = 2 if overlap else 1.  Row r of
+ *   batch b holds the compressor projections of absolute token pos0[b] + r.
+ *   With overlap (C4A), channels [0,d) of a token feed the NEXT entry and
+ *   channels [d,2d) feed the token's own entry.  A rolling [2*ratio, 2*d]
+ *   state buffer whose pre half holds the previous group is a valid argument
+ *   (L = 2*ratio, pos0 = first token of the previous group).
+ * gamma: [d] RMSNorm gain.  cache: [B, N_cap, d]; only rows of completed
+ *   entries are written.  pos0: [B] device int32.
+ * Entry g (tokens [g*ratio, g*ratio+ratio)) is written iff all its tokens
+ *   lie in the buffer and, with overlap, g == 0 or the previous group's
+ *   tokens do too, and g < N_cap.  For every channel c the entry's slots
+ *   are weighted by a softmax of their scores over the token axis (missing
+ *   previous-group slots of entry 0 get weight 0), summed, then the row is
+ *   RMS-normalised (eps) and scaled by gamma, and its last rope_dim dims are
+ *   rotated (interleaved pairs, base rope_base) at position g*ratio.
+ * Requires: 1 <= d <= 512, d even, 0 <= rope_dim <= d, rope_dim even,
+ *   ratio >= 1, L >= 1, B >= 1, N_cap >= 1.
+ */
+int csa_compress(const void* kv_state, const void* score_state, const float* gamma, void* cache,
+                 const int32_t* pos0, int B, int L, int d, int rope_dim, int ratio, int overlap, int N_cap,
+                 float eps, float rope_base, int dtype, csa_stream_t stream);
+
+/*
+ * csa_index_scores -- indexer scores, [P1] "少读 KV 之前，Indexer 仍要给历史打分";
+ * [P5] 2.2.
+ *
+ * q_idx: [B, S, Hi, di]; w: [B, S, Hi] fp32 signed per-head weights, already
+ *   scaled (1/sqrt(di)/sqrt(Hi) in the model); idx_cache: [B, N_cap, di];
+ *   q_pos: [B] device int32, query s of batch b sits at q_pos[b] + s.
+ * scores: [B, S, N_cap] fp32 output.  For entry e < nvis = min((t+1)/ratio,
+ *   N_cap): sum_h w[h] * ReLU(q_idx[h] . idx_cache[e]); entries e >= nvis
+ *   are set to -inf.
+ * Requires: Hi >= 1, di >= 1, S >= 1.
+ */
+int csa_index_scores(const void* q_idx, const float* w, const void* idx_cache, const int32_t* q_pos, float* scores,
+                     int B, int S, int Hi, int di, int N_cap, int ratio, unsigned flags, int dtype,
+                     csa_stream_t stream);
+
+/*
+ * csa_topk -- keeps at most k compressed entries per query, [P5] 2
+ * ("保留<=topK个压缩token") and 2.2.
+ *
+ * scores: [B, S, N_cap] fp32; only entries e < nvis (same rule as above) are
+ *   candidates.  topk_idx: [B, S, k] int32 output: the min(k, nvis) entries
+ *   with the largest scores (ties go to the lower entry index), in no
+ *   particular order, then -1 in the remaining slots.  topk_score: [B, S, k]
+ *   fp32 output of the matching scores (-inf on padding), may be NULL.
+ * workspace: device scratch of csa_topk_workspace_size() bytes (may be NULL
+ *   when that size is 0).
+ * Requires: 1 <= k <= 4096.
+ */
+size_t csa_topk_workspace_size(int B, int S, int N_cap, int k);
+int csa_topk(const float* scores, const int32_t* q_pos, int32_t* topk_idx, float* topk_score, void* workspace,
+             size_t workspace_bytes, int B, int S, int N_cap, int k, int ratio, csa_stream_t stream);
+
+/*
+ * csa_index_topk -- csa_index_scores followed by csa_topk.  The score buffer
+ * ([P1]: the query x candidate score buffer is temporary memory) lives at the
+ * start of `workspace` as [B, S, N_cap] fp32 and holds the scores afterwards.
+ */
+size_t csa_index_topk_workspace_size(int B, int S, int N_cap, int k);
+int csa_index_topk(const void* q_idx, const float* w, const void* idx_cache, const int32_t* q_pos,
+                   int32_t* topk_idx, float* topk_score, void* workspace, size_t workspace_bytes, int B, int S,
+                   int Hi, int di, int N_cap, int k, int ratio, unsigned flags, int dtype, csa_stream_t stream);
+
+/*
+ * csa_sparse_attn -- multi-query attention over the window plus the selected
+ * compressed entries, [P1] "局部和压缩记忆，共用一次归一化" (one candidate set, one
+ * softmax, per-head sink adds to the denominator only), "输出投影也分组…"
+ * (o = inverse_RoPE(o)); [P5] 2 (window ring, <= window+topK reads) and 2.3
+ * (sink, MQA, de-rotation).
+ *
+ * q: [B, S, H, D] (already normalised and rotated); cmp_cache: [B, N_cap, D];
+ * topk_idx: [B, S, k] int32 (entries < 0 or >= N_cap are skipped);
+ * win_kv: [B, W_cap, D] window rows.  With win_pos0 == NULL the window is a
+ *   ring: position u lives in row u % W_cap.  Otherwise row u - win_pos0[b].
+ * sink: [H] fp32 logits; q_pos: [B] device int32.
+ * out: [B, S, H, D]; lse: [B, S, H] fp32 log of the softmax denominator
+ *   (sink included), may be NULL.
+ * For query position t, the candidates are the window rows of positions
+ *   [max(0, t-window+1), t] and the listed entries; logit = softmax_scale *
+ *   (q_h . row); o_h = sum exp(logit) row / (sum exp(logit) + exp(sink_h));
+ *   the last rope_dim dims of o_h are rotated back by position t.  The same
+ *   row is key and value.
+ * Requires: 1 <= window <= W_cap (ring mode), D <= 512, D even, rope_dim
+ *   even <= D, k >= 0.  The MFMA path runs for dtype CSA_BF16, D == 512 and
+ *   H % 16 == 0; other shapes use a vector-ALU kernel.
+ */
+size_t csa_attn_workspace_size(int B, int S, int H, int D, int n_cand);
+int csa_sparse_attn(const void* q, const void* cmp_cache, const int32_t* topk_idx, const void* win_kv,
+                    const int32_t* win_pos0, const float* sink, const int32_t* q_pos, void* out, float* lse,
+                    void* workspace, size_t workspace_bytes, int B, int S, int H, int D, int rope_dim, int N_cap,
+                    int k, int W_cap, int window, float softmax_scale, float rope_base, int dtype,
+                    csa_stream_t stream);
+
+/*
+ * hca_attn -- as csa_sparse_attn, but the compressed candidates are ALL
+ * entries e < min((t+1)/ratio, N_cap) (HCA has no indexer, [P5] 3).
+ */
+int hca_attn(const void* q, const void* cmp_cache, const void* win_kv, const int32_t* win_pos0, const float* sink,
+             const int32_t* q_pos, void* out, float* lse, void* workspace, size_t workspace_bytes, int B, int S,
+             int H, int D, int rope_dim, int N_cap, int ratio, int W_cap, int window, float softmax_scale,
+             float rope_base, int dtype, csa_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CSA_H */

@@ -1,0 +1,163 @@
+"""GPU parity: every libcsa entry point against the fp64 oracle, stage by stage
+on identical inputs and end to end, at sizes the oracle finishes in seconds
+(several tiles, ragged tails, edge cases).  Calls go through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+from compressed_sparse_attention_c4a_amd import binding as K
+from compressed_sparse_attention_c4a_amd import path as P
+from compressed_sparse_attention_c4a_amd import workloads as W
+from parity import (SCORE_TOL, TOL, assert_close, check_topk_sets, raw_np, to_np)
+
+pytestmark = pytest.mark.gpu
+
+
+def _with_positions(inp, q_pos, state_back=7):
+    """Give every batch row its own query position (ragged contexts)."""
+    inp = dict(inp)
+    q_pos = np.asarray(q_pos, dtype=np.int32)
+    inp["q_pos"] = q_pos
+    sh = inp["shape"]
+    inp["state_pos0"] = (q_pos - state_back).astype(np.int32) if sh.S == 1 else inp["state_pos0"]
+    return inp
+
+
+def _cases():
+    c = {}
+    c["tiny_fp32"] = W.tiny_fp32()
+    sh = W.Shape(name="csa_decode_small", B=3, S=1, N_cap=700, window=128, W_cap=128, state_len=8, k=64, seed=11)
+    c["csa_decode_ragged_bf16"] = _with_positions(W.generate(sh), [2799, 2000, 1235])
+    sh = W.Shape(name="csa_decode_short", B=3, S=1, N_cap=64, window=128, W_cap=128, state_len=8, k=64, seed=12)
+    c["csa_decode_short_ctx_bf16"] = _with_positions(W.generate(sh), [200, 2, 71])   # nvis < k, nvis == 0, t < window
+    sh = W.Shape(name="csa_prefill_small", B=1, S=37, q_pos=130, N_cap=64, window=128, W_cap=37 + 127,
+                 win_linear=True, win_pos0=130 - 127, state_pos0=128, state_len=39, k=16, seed=13)
+    c["csa_prefill_small_bf16"] = W.generate(sh)
+    sh = W.Shape(name="hca_small", B=2, S=1, ratio=128, overlap=False, N_cap=8, window=128, W_cap=128,
+                 state_len=128, indexer=False, seed=14)
+    c["hca_decode_small_bf16"] = _with_positions(W.generate(sh), [639, 1023], state_back=127)
+    sh = W.Shape(name="csa_decode_fp32", B=2, S=1, H=16, D=128, rope=32, N_cap=300, window=16, W_cap=16,
+                 state_len=8, Hi=4, di=64, idx_rope=16, k=40, dtype="fp32", seed=15)
+    c["csa_decode_fp32"] = _with_positions(W.generate(sh), [1199, 503])
+    return c
+
+
+CASES = _cases()
+
+
+def _dt(sh):
+    return "fp32" if sh.dtype == "fp32" else "bf16"
+
+
+@pytest.fixture(scope="module", params=sorted(CASES))
+def case(request, orc):
+    inp = CASES[request.param]
+    ref = orc.pipeline(inp)
+    return request.param, inp, ref
+
+
+def test_compress_stage(case, orc):
+    name, inp, ref = case
+    sh = inp["shape"]
+    dev = P.to_device(inp)
+    K.csa_compress(dev["kv_state"], dev["score_state"], dev["gamma"], dev["cmp_cache"], dev["state_pos0"],
+                   ratio=sh.ratio, overlap=sh.overlap, rope_dim=sh.rope)
+    got = to_np(dev["cmp_cache"])
+    wr = ref["written"]
+    if wr.any():
+        assert_close(got[wr], ref["cmp_vals"][wr], TOL[_dt(sh)], f"{name}: compressed rows")
+    # rows that are not complete stay untouched
+    np.testing.assert_array_equal(raw_np(dev["cmp_cache"])[~wr], inp["cmp_cache"][~wr])
+    if sh.indexer:
+        K.csa_compress(dev["idx_kv_state"], dev["idx_score_state"], dev["idx_gamma"], dev["idx_cache"],
+                       dev["state_pos0"], ratio=sh.ratio, overlap=True, rope_dim=sh.idx_rope)
+        iw = ref["idx_written"]
+        if iw.any():
+            assert_close(to_np(dev["idx_cache"])[iw], ref["idx_vals"][iw], TOL[_dt(sh)], f"{name}: index rows")
+        np.testing.assert_array_equal(raw_np(dev["idx_cache"])[~iw], inp["idx_cache"][~iw])
+
+
+def test_index_score_stage(case, orc):
+    name, inp, ref = case
+    sh = inp["shape"]
+    if not sh.indexer:
+        pytest.skip("HCA has no indexer")
+    dev = P.to_device(inp)
+    idx_cache = P._dev(ref["idx_cache"], "cuda")          # the oracle's compressed index rows
+    scores = torch.empty((sh.B, sh.S, sh.N_cap), dtype=torch.float32, device="cuda")
+    K.csa_index_scores(dev["q_idx"], dev["w"], idx_cache, dev["q_pos"], scores, ratio=sh.ratio)
+    got = scores.cpu().numpy().astype(np.float64)
+    exp = ref["scores"]
+    vis = np.isfinite(exp)
+    np.testing.assert_array_equal(np.isfinite(got), vis)     # visibility is exact
+    if vis.any():
+        assert_close(got[vis], exp[vis], SCORE_TOL[_dt(sh)], f"{name}: index scores")
+
+
+def test_topk_stage_exact_on_identical_scores(case, orc):
+    name, inp, ref = case
+    sh = inp["shape"]
+    if not sh.indexer:
+        pytest.skip("HCA has no indexer")
+    s32 = ref["scores"].astype(np.float32)
+    s64 = s32.astype(np.float64)                    # both sides decide on the same fp32 scores
+    o_idx, _ = orc.topk(s64, ref["nvis"], sh.k)
+    scores = torch.from_numpy(s32).cuda()
+    idx = torch.empty((sh.B, sh.S, sh.k), dtype=torch.int32, device="cuda")
+    val = torch.empty((sh.B, sh.S, sh.k), dtype=torch.float32, device="cuda")
+    K.csa_topk(scores, torch.from_numpy(inp["q_pos"]).cuda(), idx, val, ratio=sh.ratio)
+    gi = idx.cpu().numpy()
+    check_topk_sets(gi, o_idx, s64, ref["nvis"], sh.k, exact=True)
+    gv = val.cpu().numpy()
+    for qi, (row_i, row_v) in enumerate(zip(gi.reshape(-1, sh.k), gv.reshape(-1, sh.k))):
+        m = row_i >= 0
+        np.testing.assert_array_equal(row_v[m], s32.reshape(-1, sh.N_cap)[qi, row_i[m]])
+
+
+def test_attention_stage(case, orc):
+    name, inp, ref = case
+    sh = inp["shape"]
+    dev = P.to_device(inp)
+    cmp = P._dev(ref["cmp_cache"], "cuda")
+    out = torch.empty_like(dev["q"])
+    lse = torch.empty((sh.B, sh.S, sh.H), dtype=torch.float32, device="cuda")
+    if sh.indexer:
+        topk = torch.from_numpy(ref["topk_idx"]).cuda()
+        K.csa_sparse_attn(dev["q"], cmp, topk, dev["win_kv"], dev.get("win_pos0"), dev["sink"], dev["q_pos"], out,
+                          lse, rope_dim=sh.rope, window=sh.window)
+    else:
+        K.hca_attn(dev["q"], cmp, dev["win_kv"], dev.get("win_pos0"), dev["sink"], dev["q_pos"], out, lse,
+                   ratio=sh.ratio, rope_dim=sh.rope, window=sh.window)
+    assert_close(to_np(out), ref["out"], TOL[_dt(sh)], f"{name}: attention output")
+    assert_close(lse.cpu().numpy(), ref["lse"], TOL["fp32"] if sh.dtype == "fp32" else 1e-3, f"{name}: lse")
+
+
+def test_end_to_end(case, orc):
+    name, inp, ref = case
+    sh = inp["shape"]
+    dev = P.to_device(inp)
+    step = P.Step(dev)
+    out = step.run(dev)
+    torch.cuda.synchronize()
+    tol = TOL[_dt(sh)]
+    wr = ref["written"]
+    if wr.any():
+        assert_close(to_np(dev["cmp_cache"])[wr], ref["cmp_vals"][wr], tol, f"{name}: compressed rows")
+    if sh.indexer:
+        gi = step.topk_idx.cpu().numpy()
+        check_topk_sets(gi, ref["topk_idx"], ref["scores"], ref["nvis"], sh.k)
+        # attention of the oracle on the GPU's own selection (a legitimate tie swap is not an error)
+        o2, _, _ = orc.attn(inp["q"], ref["cmp_cache"], inp["win_kv"], inp["sink"], inp["q_pos"], topk_idx=gi,
+                            ratio=sh.ratio, win_pos0=inp.get("win_pos0"), window=sh.window, rope_dim=sh.rope)
+        assert_close(to_np(out), o2, tol, f"{name}: output")
+    else:
+        assert_close(to_np(out), ref["out"], tol, f"{name}: output")
+
+
+def test_repeat_runs_are_bitwise_identical(case):
+    name, inp, _ = case
+    dev = P.to_device(inp)
+    step = P.Step(dev)
+    a = raw_np(step.run(dev)).copy()
+    b = raw_np(step.run(dev))
+    np.testing.assert_array_equal(a, b)

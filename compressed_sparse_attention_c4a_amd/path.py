@@ -50,20 +50,47 @@ class Step:
             aws = K.csa_attn_workspace_size(sh.B, sh.S, sh.H, sh.D, sh.window + sh.N_cap)
         self.attn_ws = torch.empty(max(aws, 1), dtype=torch.uint8, device=device) if aws else None
 
-    def run(self, dev: dict, stream=None):
+    def calls(self, dev: dict, stream=None):
+        """The pass as a list of (name, thunk), in launch order."""
         sh = self.sh
-        K.csa_compress(dev["kv_state"], dev["score_state"], dev["gamma"], dev["cmp_cache"], dev["state_pos0"],
-                       ratio=sh.ratio, overlap=sh.overlap, rope_dim=sh.rope, stream=stream)
+        c = [("compress", lambda: K.csa_compress(dev["kv_state"], dev["score_state"], dev["gamma"], dev["cmp_cache"],
+                                                 dev["state_pos0"], ratio=sh.ratio, overlap=sh.overlap,
+                                                 rope_dim=sh.rope, stream=stream))]
         if sh.indexer:
-            K.csa_compress(dev["idx_kv_state"], dev["idx_score_state"], dev["idx_gamma"], dev["idx_cache"],
-                           dev["state_pos0"], ratio=sh.ratio, overlap=True, rope_dim=sh.idx_rope, stream=stream)
-            K.csa_index_topk(dev["q_idx"], dev["w"], dev["idx_cache"], dev["q_pos"], self.topk_idx,
-                             ratio=sh.ratio, workspace=self.idx_ws, stream=stream)
-            K.csa_sparse_attn(dev["q"], dev["cmp_cache"], self.topk_idx, dev["win_kv"], dev.get("win_pos0"),
-                              dev["sink"], dev["q_pos"], self.out, self.lse, rope_dim=sh.rope, window=sh.window,
-                              workspace=self.attn_ws, stream=stream)
+            c.append(("compress_idx", lambda: K.csa_compress(dev["idx_kv_state"], dev["idx_score_state"],
+                                                             dev["idx_gamma"], dev["idx_cache"], dev["state_pos0"],
+                                                             ratio=sh.ratio, overlap=True, rope_dim=sh.idx_rope,
+                                                             stream=stream)))
+            c.append(("index_topk", lambda: K.csa_index_topk(dev["q_idx"], dev["w"], dev["idx_cache"], dev["q_pos"],
+                                                             self.topk_idx, ratio=sh.ratio, workspace=self.idx_ws,
+                                                             stream=stream)))
+            c.append(("attn", lambda: K.csa_sparse_attn(dev["q"], dev["cmp_cache"], self.topk_idx, dev["win_kv"],
+                                                        dev.get("win_pos0"), dev["sink"], dev["q_pos"], self.out,
+                                                        self.lse, rope_dim=sh.rope, window=sh.window,
+                                                        workspace=self.attn_ws, stream=stream)))
         else:
-            K.hca_attn(dev["q"], dev["cmp_cache"], dev["win_kv"], dev.get("win_pos0"), dev["sink"], dev["q_pos"],
-                       self.out, self.lse, ratio=sh.ratio, rope_dim=sh.rope, window=sh.window,
-                       workspace=self.attn_ws, stream=stream)
+            c.append(("attn", lambda: K.hca_attn(dev["q"], dev["cmp_cache"], dev["win_kv"], dev.get("win_pos0"),
+                                                 dev["sink"], dev["q_pos"], self.out, self.lse, ratio=sh.ratio,
+                                                 rope_dim=sh.rope, window=sh.window, workspace=self.attn_ws,
+                                                 stream=stream)))
+        return c
+
+    def run(self, dev: dict, stream=None):
+        for _, fn in self.calls(dev, stream):
+            fn()
+        return self.out
+
+    def run_timed(self, dev: dict, stream, events: dict):
+        """As run(); calls named in `events` are bracketed by timing events
+        recorded on `stream` (the stream the kernels are launched on)."""
+        for name, fn in self.calls(dev, stream):
+            if name in events:
+                a = torch.cuda.Event(enable_timing=True)
+                b = torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                fn()
+                b.record(stream)
+                events[name].append((a, b))
+            else:
+                fn()
         return self.out

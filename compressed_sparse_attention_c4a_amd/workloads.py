@@ -214,3 +214,15 @@ def algorithmic_bytes_per_query(sh: Shape) -> dict:
         out["attn"] = reads * sh.D * e + 2 * sh.H * sh.D * e
     out["reads"] = reads
     return out
+
+
+def slice_batch(inp: dict, n: int) -> dict:
+    """The first n batch rows of a generated workload (pure slicing)."""
+    sh = dataclasses.replace(inp["shape"], B=n)
+    out = {"shape": sh}
+    per_head = {"sink", "gamma", "idx_gamma"}
+    for key, val in inp.items():
+        if key == "shape":
+            continue
+        out[key] = val if (val is None or key in per_head) else val[:n]
+    return out

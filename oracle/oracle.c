@@ -409,3 +409,15 @@ int orc_attn(const void* q, int qdt, const void* cmp_cache, int cdt, const int32
     }
   return bad ? -1 : 0;
 }
+
+/* Threads an OpenMP region of this library uses (for reporting CPU timings). */
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+int orc_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}

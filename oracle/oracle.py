@@ -64,8 +64,15 @@ def lib():
         L.orc_attn.argtypes = [vp, i32, vp, i32, vp, i32, i32, vp, i32, vp, vp, vp, vp, vp, vp,
                                i32, i32, i32, i32, i32, i32, i32, i32, dbl, dbl]
         L.orc_attn.restype = i32
+        L.orc_num_threads.argtypes = []
+        L.orc_num_threads.restype = i32
         _lib = L
     return _lib
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    return int(lib().orc_num_threads())
 
 
 def _dt(a: np.ndarray) -> int:

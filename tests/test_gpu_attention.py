@@ -1,0 +1,103 @@
+"""GPU parity of the attention entry points on shapes that select each
+kernel variant (head groups of 16, 32 and 64 heads per workgroup), in sparse
+(CSA) and dense (HCA) mode, with ring and linear windows, -1 padding anywhere
+in the selection, short contexts and ragged tile tails."""
+import numpy as np
+import pytest
+import torch
+
+from compressed_sparse_attention_c4a_amd import binding as K
+from compressed_sparse_attention_c4a_amd import workloads as W
+from parity import TOL, assert_close, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(seed, B, S, H, N_cap, W_cap, k, q_pos, linear=False, D=512, dtype="bf16"):
+    dr = W.Draw(seed)
+    q = dr.data((B, S, H, D), dtype)
+    cmp = dr.data((B, N_cap, D), dtype)
+    win = dr.data((B, W_cap, D), dtype)
+    sink = dr.f32((H,))
+    rng = np.random.default_rng(seed + 1000)
+    q_pos = np.asarray(q_pos, dtype=np.int32)
+    topk = np.full((B, S, k), -1, dtype=np.int32)
+    for b in range(B):
+        for s in range(S):
+            nv = min((int(q_pos[b]) + s + 1) // 4, N_cap)
+            m = min(k, nv)
+            if m:
+                sel = rng.choice(nv, size=m, replace=False).astype(np.int32)
+                slots = rng.choice(k, size=m, replace=False)     # padding scattered through the list
+                topk[b, s, slots] = sel
+    win_pos0 = (q_pos - (W_cap - S)).astype(np.int32) if linear else None
+    return dict(q=q, cmp=cmp, win=win, sink=sink, q_pos=q_pos, topk=topk, win_pos0=win_pos0)
+
+
+def _dev(a):
+    if a is None:
+        return None
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a).cuda().view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+VARIANTS = {
+    # name: (B, S, H, N_cap, W_cap, k, q_pos, linear window, window)
+    "hg16_decode": (5, 1, 128, 600, 128, 96, [2399, 1000, 130, 7, 0], False, 128),
+    "hg32_decode": (64, 1, 128, 300, 128, 40, list(range(400, 1040, 10)), False, 128),
+    "hg64_prefill": (1, 160, 128, 200, 160 + 127, 48, [600], True, 128),
+    "hg16_h48": (3, 1, 48, 100, 64, 33, [399, 250, 60], False, 64),
+    "hg32_h96_window_gt_ctx": (100, 1, 96, 64, 128, 20, list(range(0, 200, 2)), False, 128),
+}
+
+
+@pytest.mark.parametrize("name", sorted(VARIANTS))
+@pytest.mark.parametrize("dense", [False, True])
+def test_attention_variants(orc, name, dense):
+    B, S, H, N_cap, W_cap, k, q_pos, linear, window = VARIANTS[name]
+    x = _inputs(hash(name) % 1000, B, S, H, N_cap, W_cap, k, q_pos, linear)
+    out = torch.empty((B, S, H, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, S, H), dtype=torch.float32, device="cuda")
+    if dense:
+        K.hca_attn(_dev(x["q"]), _dev(x["cmp"]), _dev(x["win"]), _dev(x["win_pos0"]), _dev(x["sink"]),
+                   _dev(x["q_pos"]), out, lse, ratio=4, rope_dim=64, window=window)
+        ref, rlse, _ = orc.attn(x["q"], x["cmp"], x["win"], x["sink"], x["q_pos"], topk_idx=None, ratio=4,
+                                win_pos0=x["win_pos0"], window=window, rope_dim=64)
+    else:
+        K.csa_sparse_attn(_dev(x["q"]), _dev(x["cmp"]), _dev(x["topk"]), _dev(x["win"]), _dev(x["win_pos0"]),
+                          _dev(x["sink"]), _dev(x["q_pos"]), out, lse, rope_dim=64, window=window)
+        ref, rlse, _ = orc.attn(x["q"], x["cmp"], x["win"], x["sink"], x["q_pos"], topk_idx=x["topk"],
+                                win_pos0=x["win_pos0"], window=window, rope_dim=64)
+    torch.cuda.synchronize()
+    assert_close(to_np(out), ref, TOL["bf16"], f"{name} dense={dense}: output")
+    assert_close(lse.cpu().numpy(), rlse, 1e-3, f"{name} dense={dense}: lse")
+
+
+def test_sparse_with_every_visible_entry_equals_dense():
+    B, S, H, N_cap = 4, 1, 128, 256
+    x = _inputs(7, B, S, H, N_cap, 128, 256, [1023, 700, 300, 40])
+    topk = np.full((B, S, 256), -1, dtype=np.int32)
+    for b in range(B):
+        nv = min((int(x["q_pos"][b]) + 1) // 4, N_cap)
+        topk[b, 0, :nv] = np.arange(nv)
+    o1 = torch.empty((B, S, H, 512), dtype=torch.bfloat16, device="cuda")
+    o2 = torch.empty_like(o1)
+    K.csa_sparse_attn(_dev(x["q"]), _dev(x["cmp"]), _dev(topk), _dev(x["win"]), None, _dev(x["sink"]),
+                      _dev(x["q_pos"]), o1, rope_dim=64, window=128)
+    K.hca_attn(_dev(x["q"]), _dev(x["cmp"]), _dev(x["win"]), None, _dev(x["sink"]), _dev(x["q_pos"]), o2, ratio=4,
+               rope_dim=64, window=128)
+    # same candidates in the same order: the two kernels must agree bit for bit
+    assert torch.equal(o1, o2)
+
+
+def test_sink_minus_infinity_and_no_rope(orc):
+    B, S, H = 2, 1, 64
+    x = _inputs(9, B, S, H, 50, 128, 16, [199, 150])
+    sink = np.full((H,), -np.inf, dtype=np.float32)
+    out = torch.empty((B, S, H, 512), dtype=torch.bfloat16, device="cuda")
+    K.csa_sparse_attn(_dev(x["q"]), _dev(x["cmp"]), _dev(x["topk"]), _dev(x["win"]), None, _dev(sink),
+                      _dev(x["q_pos"]), out, rope_dim=0, window=128, softmax_scale=0.03)
+    ref, _, _ = orc.attn(x["q"], x["cmp"], x["win"], sink, x["q_pos"], topk_idx=x["topk"], window=128, rope_dim=0,
+                         scale=0.03)
+    assert_close(to_np(out), ref, TOL["bf16"], "no sink, no rope")

@@ -27,11 +27,22 @@ struct Elt;
 template <>
 struct Elt<float> {
   static __device__ __forceinline__ float ld(const float* p, size_t i) { return p[i]; }
+  // two adjacent elements (i even)
+  static __device__ __forceinline__ void ld2(const float* p, size_t i, float& a, float& b) {
+    const float2 v = *(const float2*)(p + i);
+    a = v.x;
+    b = v.y;
+  }
   static __device__ __forceinline__ void st(float* p, size_t i, float v) { p[i] = v; }
 };
 template <>
 struct Elt<bf16> {
   static __device__ __forceinline__ float ld(const bf16* p, size_t i) { return bf2f(p[i].x); }
+  static __device__ __forceinline__ void ld2(const bf16* p, size_t i, float& a, float& b) {
+    const uint32_t v = *(const uint32_t*)(p + i);
+    a = __uint_as_float(v << 16);
+    b = __uint_as_float(v & 0xFFFF0000u);
+  }
   static __device__ __forceinline__ void st(bf16* p, size_t i, float v) { p[i].x = f2bf(v); }
 };
 
@@ -66,6 +77,64 @@ __device__ __forceinline__ int xcd_remap(int L, int total) {
   const int per = total / 8, rem = total % 8;
   const int x = L % 8, j = L / 8;
   return x * per + (x < rem ? x : rem) + j;
+}
+
+// ---------------------------------------------------------------------------
+// Direct global -> LDS copies (gfx950 global_load_lds_dwordx4): each lane's 16
+// bytes land at lds_wave_base + 16 * lane.  The copy is issued from inline asm
+// on purpose: the compiler's wait-count pass cannot tell which LDS buffer an
+// in-flight copy targets and would otherwise put vmcnt(0) before unrelated LDS
+// reads, draining every prefetch.  The asm writes no VGPR (its destination is
+// LDS through M0, saved and restored here), so nothing in a register can be
+// overwritten while the copy is in flight.  Callers wait for completion with
+// WAIT_VMCNT before reading the data; compiler-inserted waits for ordinary
+// loads stay correct because unseen copies only make them stricter.
+__device__ __forceinline__ void dma16(const void* gaddr, const void* lds_wave_base) {
+  // the LDS base is wave-uniform by contract; readfirstlane puts it in an SGPR for M0
+  const uint32_t m = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) void*)lds_wave_base));
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(gaddr), "s"(m)
+      : "memory");
+}
+
+// Same copy with a wave-uniform 64-bit base (SGPRs) and a per-lane 32-bit
+// byte offset: no per-lane address arithmetic at the call site.
+__device__ __forceinline__ void dma16_sbase(const void* sbase, uint32_t lane_off, const void* lds_wave_base) {
+  const uint32_t m = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) void*)lds_wave_base));
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(lane_off), "s"(sbase), "s"(m)
+      : "memory");
+}
+
+// s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt[3:0], expcnt
+// [6:4] = 7, lgkmcnt [11:8] = 15, vmcnt[5:4] in [15:14]).
+#define WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt((((n)&15) | (((n) >> 4) << 14)) | 0x0F70)
+
+// Workgroup barrier for LDS traffic only: this wave's LDS reads/writes are
+// complete (lgkmcnt 0) and the compiler may not move memory accesses across
+// it.  Copies in flight are not waited for (explicit vmcnt waits track them);
+// __syncthreads() would drain them through its release fence.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt unconstrained
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
 }
 
 __device__ __forceinline__ float wave_sum(float v) {

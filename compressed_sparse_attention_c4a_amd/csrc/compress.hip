@@ -38,37 +38,52 @@ __global__ __launch_bounds__(256) void compress_kernel(const T* __restrict__ kv,
   const bool active = 2 * p < d;
   float y[2] = {0.f, 0.f};
   if (active) {
+    // Slots are processed in chunks of 16 whose loads are all issued before
+    // any of them is used, so the memory latency is paid once per chunk.
+    constexpr int CH = 16;
+    const int nslot = overlap ? 2 * ratio : ratio;
+    float mx[2] = {-INFINITY, -INFINITY}, den[2] = {0.f, 0.f}, num[2] = {0.f, 0.f};
+    for (int j0 = 0; j0 < nslot; j0 += CH) {
+      float sv[CH][2], vv[CH][2];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int c = 2 * p + h;
-      float mx = -INFINITY, den = 0.f, num = 0.f;
-      const int nslot = overlap ? 2 * ratio : ratio;
-      for (int j = 0; j < nslot; ++j) {
+      for (int jj = 0; jj < CH; ++jj) {
+        const int j = j0 + jj;
+        sv[jj][0] = sv[jj][1] = -INFINITY;
+        vv[jj][0] = vv[jj][1] = 0.f;
+        if (j >= nslot) continue;
         long tok;
         int ch;
         if (overlap && j < ratio) {
           if (g == 0) continue;  // missing previous group: weight 0
           tok = first - ratio + j;
-          ch = c;
+          ch = 2 * p;
         } else {
           tok = first + (overlap ? j - ratio : j);
-          ch = overlap ? d + c : c;
+          ch = overlap ? d + 2 * p : 2 * p;
         }
         const size_t off = (size_t)(tok - p0) * row_w + ch;
-        const float s = Elt<T>::ld(scb, off);
-        const float v = Elt<T>::ld(kvb, off);
-        if (s > mx) {
-          const float r = expf(mx - s);
-          den *= r;
-          num *= r;
-          mx = s;
-        }
-        const float e = expf(s - mx);
-        den += e;
-        num += e * v;
+        Elt<T>::ld2(scb, off, sv[jj][0], sv[jj][1]);
+        Elt<T>::ld2(kvb, off, vv[jj][0], vv[jj][1]);
       }
-      y[h] = num / den;
+#pragma unroll
+      for (int jj = 0; jj < CH; ++jj)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const float sj = sv[jj][h];
+          if (sj == -INFINITY) continue;
+          if (sj > mx[h]) {
+            const float r = expf(mx[h] - sj);
+            den[h] *= r;
+            num[h] *= r;
+            mx[h] = sj;
+          }
+          const float e = expf(sj - mx[h]);
+          den[h] += e;
+          num[h] += e * vv[jj][h];
+        }
     }
+    y[0] = num[0] / den[0];
+    y[1] = num[1] / den[1];
   }
 
   // RMSNorm over the d channels of the entry.

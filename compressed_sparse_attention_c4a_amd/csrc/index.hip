@@ -46,35 +46,32 @@ __global__ __launch_bounds__(256) void index_scores_generic(const T* __restrict_
 // MFMA kernel (bf16, di == 128, Hi == 16*MT).  HBM-bound streaming of the
 // index cache: every candidate row (256 B) is read once per query.
 //
-// Workgroup = 4 waves, one query, a chunk of 4*T tiles of 64 candidates
+// Workgroup = 4 waves, one query, a chunk of 4*T tiles of 32 candidates
 // (tiles interleaved across the waves so the group streams contiguous rows).
-// Per wave and tile: 16 direct global->LDS loads (1 KiB each, 4 rows) into a
-// private double buffer, prefetching tile i+1 while tile i is scored.
-// Scores: v_mfma_f32_16x16x32_bf16 with A = q_idx (M = 16 heads, K = 32 dims,
-// kept in VGPRs for the whole kernel) and B = k^T read from LDS (N = 16
-// candidates); C lane l holds heads 4*(l/16)+i of candidate l%16, so the
-// ReLU * w head reduction is in-lane over 4*MT values plus two cross-lane
-// steps.  LDS rows are XOR-swizzled (16-byte granule c of row r sits at c ^ (r
-// & 15)) so the 16 rows a quarter-wave reads fall in distinct banks.
+// Per wave and tile: 8 direct global->LDS copies (1 KiB each, 4 rows) into a
+// private double buffer, tile i+1 in flight while tile i is scored; 80 KiB of
+// LDS lets two workgroups share a CU.  Scores: v_mfma_f32_16x16x32_bf16 with
+// A = q_idx (M = 16 heads, K = 32 dims, kept in VGPRs for the whole kernel)
+// and B = k^T from LDS (N = 16 candidates); C lane l holds heads 4*(l/16)+i
+// of candidate l%16, so the ReLU * w head reduction is in-lane over 4*MT
+// values plus two cross-lane steps.  LDS rows are XOR-swizzled (16-byte
+// granule c of row r sits at c ^ (r & 15)) so the 16 rows a quarter-wave
+// reads fall in distinct banks.
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int IX_TILE = 64;           // candidates per wave tile
+constexpr int IX_TILE = 32;           // candidates per wave tile
 constexpr int IX_WAVES = 4;
 constexpr int IX_ROW = 256;           // bytes per index row (128 bf16)
 constexpr int IX_TILE_BYTES = IX_TILE * IX_ROW;
+constexpr int IX_COPIES = IX_TILE_BYTES / 1024;  // 1 KiB copies per tile and wave
 
-#define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
-
-// s_waitcnt with only vmcnt limited (gfx9 encoding: vmcnt[3:0] | expcnt 7 | lgkmcnt 15 | vmcnt[5:4]).
-#define WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt((((n)&15) | (((n) >> 4) << 14)) | 0x0F70)
-
-template <int MT, int T>
+template <int MT>
 __global__ __launch_bounds__(256) void index_scores_mfma(const bf16* __restrict__ q, const float* __restrict__ w,
                                                          const bf16* __restrict__ K,
                                                          const int32_t* __restrict__ q_pos,
                                                          float* __restrict__ scores, int S, int N_cap, int ratio,
-                                                         unsigned flags, int chunks) {
+                                                         unsigned flags, int T, int chunks) {
   constexpr int HI = 16 * MT;
   __shared__ __attribute__((aligned(16))) uint8_t lds_q[HI * IX_ROW];
   __shared__ __attribute__((aligned(16))) uint8_t lds_k[IX_WAVES][2][IX_TILE_BYTES];
@@ -83,7 +80,8 @@ __global__ __launch_bounds__(256) void index_scores_mfma(const bf16* __restrict_
   const int b = qi / S, s = qi % S;
   const long t = (long)q_pos[b] + s;
   const int nv = (int)visible_entries(t, ratio, N_cap);
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
   const int g = lane >> 4, n = lane & 15;
   const int e_chunk = chunk * IX_WAVES * T * IX_TILE;
   float* out = scores + (size_t)qi * N_cap;
@@ -109,38 +107,41 @@ __global__ __launch_bounds__(256) void index_scores_mfma(const bf16* __restrict_
     for (int i = 0; i < 4; ++i) wv[mt][i] = w[(size_t)qi * HI + 16 * mt + 4 * g + i];
   }
   const bool relu = !(flags & CSA_INDEX_NO_RELU);
+  // ordinary loads complete before the first tile copy (no compiler wait in
+  // the tile loop can then drain the prefetch)
+  WAIT_VMCNT(0);
 
   auto tile_e0 = [&](int i) { return e_chunk + (i * IX_WAVES + wave) * IX_TILE; };
   auto issue = [&](int i, int buf) {
     const int e0 = tile_e0(i);
 #pragma unroll
-    for (int j = 0; j < IX_TILE / 4; ++j) {
+    for (int j = 0; j < IX_COPIES; ++j) {
       const int r = 4 * j + (lane >> 4);
       const int c = (lane & 15) ^ (r & 15);
       int e = e0 + r;
       e = e < nv ? e : nv - 1;  // rows past the visible range reload a valid row (masked below)
-      __builtin_amdgcn_global_load_lds((const void*)(Kb + (size_t)e * 128 + 8 * c),
-                                       LDS_PTR(&lds_k[wave][buf][j * 1024]), 16, 0, 0);
+      dma16(Kb + (size_t)e * 128 + 8 * c, &lds_k[wave][buf][j * 1024]);
     }
   };
 
-  float sv[T];
   if (tile_e0(0) < nv) issue(0, 0);
-#pragma unroll
   for (int i = 0; i < T; ++i) {
     const int e0 = tile_e0(i);
-    const bool live = e0 < nv;  // wave-uniform
+    if (e0 >= N_cap) break;                   // wave-uniform
+    const bool live = e0 < nv;
     const bool next_live = (i + 1 < T) && tile_e0(i + 1) < nv;
     if (next_live) issue(i + 1, (i + 1) & 1);
+    // everything older than the just-issued copies is done: tile i and the
+    // previous tile's score store
     if (next_live)
-      WAIT_VMCNT(IX_TILE / 4);
+      WAIT_VMCNT(IX_COPIES);
     else
       WAIT_VMCNT(0);
     float mine = -INFINITY;
     if (live) {
       const uint8_t* kt = lds_k[wave][i & 1];
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
+      for (int nt = 0; nt < IX_TILE / 16; ++nt) {
         f32x4_t acc[MT];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -162,13 +163,7 @@ __global__ __launch_bounds__(256) void index_scores_mfma(const bf16* __restrict_
       }
       if (e0 + lane >= nv) mine = -INFINITY;
     }
-    sv[i] = mine;
-  }
-  // stores only after the last tile: no store is in flight while vmcnt tracks tile loads
-#pragma unroll
-  for (int i = 0; i < T; ++i) {
-    const int e = tile_e0(i) + lane;
-    if (e < N_cap) out[e] = sv[i];
+    if (lane < IX_TILE && e0 + lane < N_cap) out[e0 + lane] = mine;
   }
 }
 
@@ -182,28 +177,20 @@ hipError_t launch_index_scores(const void* q, const float* w, const void* K, con
                                hipStream_t st) {
   const int Q = B * S;
   if (dtype == CSA_BF16 && di == 128 && Hi % 16 == 0 && Hi <= 64) {
-    // tiles per wave: aim for >= ~2 workgroups per CU while keeping chunks long
-    int T = 4;
-    while (T > 1 && (long)Q * ((N_cap + IX_WAVES * T * IX_TILE - 1) / (IX_WAVES * T * IX_TILE)) < 512) T >>= 1;
+    // chunk = 4 waves x T tiles x 32 candidates; aim for ~1024 workgroups (two
+    // resident per CU) without chunks shorter than one tile per wave
+    const long cand = (long)Q * N_cap;
+    long per = (cand + 1023) / 1024;
+    int T = (int)((per + IX_WAVES * IX_TILE - 1) / (IX_WAVES * IX_TILE));
+    T = T < 1 ? 1 : T;
     const int chunks = (N_cap + IX_WAVES * T * IX_TILE - 1) / (IX_WAVES * T * IX_TILE);
     const dim3 grid((unsigned)((long)Q * chunks));
-    auto go = [&](auto kern) {
-      hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, (const bf16*)q, w, (const bf16*)K, q_pos, scores, S, N_cap,
-                         ratio, flags, chunks);
-    };
-#define IX_CASE(MT_)                                  \
-  case MT_:                                           \
-    if (T == 4) go(index_scores_mfma<MT_, 4>);        \
-    else if (T == 2) go(index_scores_mfma<MT_, 2>);   \
-    else go(index_scores_mfma<MT_, 1>);               \
-    break;
     switch (Hi / 16) {
-      IX_CASE(1)
-      IX_CASE(2)
-      IX_CASE(3)
-      IX_CASE(4)
+      case 1: hipLaunchKernelGGL(index_scores_mfma<1>, grid, dim3(256), 0, st, (const bf16*)q, w, (const bf16*)K, q_pos, scores, S, N_cap, ratio, flags, T, chunks); break;
+      case 2: hipLaunchKernelGGL(index_scores_mfma<2>, grid, dim3(256), 0, st, (const bf16*)q, w, (const bf16*)K, q_pos, scores, S, N_cap, ratio, flags, T, chunks); break;
+      case 3: hipLaunchKernelGGL(index_scores_mfma<3>, grid, dim3(256), 0, st, (const bf16*)q, w, (const bf16*)K, q_pos, scores, S, N_cap, ratio, flags, T, chunks); break;
+      default: hipLaunchKernelGGL(index_scores_mfma<4>, grid, dim3(256), 0, st, (const bf16*)q, w, (const bf16*)K, q_pos, scores, S, N_cap, ratio, flags, T, chunks); break;
     }
-#undef IX_CASE
     return hipGetLastError();
   }
   dim3 grid((unsigned)((N_cap + 255) / 256), (unsigned)(B * S));

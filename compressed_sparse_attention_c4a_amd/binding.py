@@ -96,47 +96,76 @@ def _check(rc: int, name: str):
         raise RuntimeError(f"{name} failed ({L.csa_error_string(rc).decode()}): {L.csa_last_error().decode()}")
 
 
+class Prepared:
+    """One library call with its arguments marshalled once.  Calling it issues
+    the same launch again (same tensors, sizes and stream), without the
+    per-call Python work of the wrappers below."""
+
+    __slots__ = ("name", "fn", "args", "keep")
+
+    def __init__(self, name, fn, args, keep=()):
+        self.name, self.fn, self.args = name, fn, args
+        self.keep = keep  # tensors the call owns (a workspace allocated here)
+
+    def __call__(self):
+        rc = self.fn(*self.args)
+        if rc != 0:
+            _check(rc, self.name)
+
+
+def _run(name: str, args: tuple, prepare: bool, keep=()):
+    fn = getattr(load(), name)
+    if prepare:
+        return Prepared(name, fn, args, keep)
+    _check(fn(*args), name)
+    return None
+
+
 # ----------------------------------------------------------------------------- entry points
+# Every entry point takes `prepare=True` to return a Prepared call instead of
+# running it.
+
+
 def csa_version() -> int:
     return load().csa_version()
 
 
 def csa_compress(kv_state, score_state, gamma, cache, pos0, *, ratio: int, overlap: bool, rope_dim: int,
-                 eps: float = 1e-6, rope_base: float = 10000.0, stream=None):
+                 eps: float = 1e-6, rope_base: float = 10000.0, stream=None, prepare: bool = False):
     B, L, md = kv_state.shape
     d = cache.shape[-1]
     if md != (2 if overlap else 1) * d or score_state.shape != kv_state.shape:
         raise ValueError("state width must be (2 if overlap else 1) * d and kv/score shapes must match")
-    dt = _dtype_code(kv_state)
-    rc = load().csa_compress(_ptr(kv_state, kv_state.dtype, "kv_state"), _ptr(score_state, kv_state.dtype, "score_state"),
-                             _ptr(gamma, torch.float32, "gamma"), _ptr(cache, kv_state.dtype, "cache"),
-                             _ptr(pos0, torch.int32, "pos0"), B, L, d, rope_dim, ratio, int(overlap), cache.shape[1],
-                             eps, rope_base, dt, _stream(stream))
-    _check(rc, "csa_compress")
+    dt = kv_state.dtype
+    args = (_ptr(kv_state, dt, "kv_state"), _ptr(score_state, dt, "score_state"), _ptr(gamma, torch.float32, "gamma"),
+            _ptr(cache, dt, "cache"), _ptr(pos0, torch.int32, "pos0"), B, L, d, rope_dim, ratio, int(overlap),
+            cache.shape[1], eps, rope_base, _dtype_code(kv_state), _stream(stream))
+    return _run("csa_compress", args, prepare)
 
 
-def csa_index_scores(q_idx, w, idx_cache, q_pos, scores, *, ratio: int, relu: bool = True, stream=None):
+def csa_index_scores(q_idx, w, idx_cache, q_pos, scores, *, ratio: int, relu: bool = True, stream=None,
+                     prepare: bool = False):
     B, S, Hi, di = q_idx.shape
     N_cap = idx_cache.shape[1]
-    rc = load().csa_index_scores(_ptr(q_idx, q_idx.dtype, "q_idx"), _ptr(w, torch.float32, "w"),
-                                 _ptr(idx_cache, q_idx.dtype, "idx_cache"), _ptr(q_pos, torch.int32, "q_pos"),
-                                 _ptr(scores, torch.float32, "scores"), B, S, Hi, di, N_cap, ratio,
-                                 0 if relu else CSA_INDEX_NO_RELU, _dtype_code(q_idx), _stream(stream))
-    _check(rc, "csa_index_scores")
+    args = (_ptr(q_idx, q_idx.dtype, "q_idx"), _ptr(w, torch.float32, "w"), _ptr(idx_cache, q_idx.dtype, "idx_cache"),
+            _ptr(q_pos, torch.int32, "q_pos"), _ptr(scores, torch.float32, "scores"), B, S, Hi, di, N_cap, ratio,
+            0 if relu else CSA_INDEX_NO_RELU, _dtype_code(q_idx), _stream(stream))
+    return _run("csa_index_scores", args, prepare)
 
 
 def csa_topk_workspace_size(B: int, S: int, N_cap: int, k: int) -> int:
     return load().csa_topk_workspace_size(B, S, N_cap, k)
 
 
-def csa_topk(scores, q_pos, topk_idx, topk_score=None, *, ratio: int, workspace=None, stream=None):
+def csa_topk(scores, q_pos, topk_idx, topk_score=None, *, ratio: int, workspace=None, stream=None,
+             prepare: bool = False):
     B, S, N_cap = scores.shape
     k = topk_idx.shape[-1]
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    rc = load().csa_topk(_ptr(scores, torch.float32, "scores"), _ptr(q_pos, torch.int32, "q_pos"),
-                         _ptr(topk_idx, torch.int32, "topk_idx"), _ptr(topk_score, torch.float32, "topk_score"),
-                         _ptr(workspace, None, "workspace"), ws_bytes, B, S, N_cap, k, ratio, _stream(stream))
-    _check(rc, "csa_topk")
+    args = (_ptr(scores, torch.float32, "scores"), _ptr(q_pos, torch.int32, "q_pos"),
+            _ptr(topk_idx, torch.int32, "topk_idx"), _ptr(topk_score, torch.float32, "topk_score"),
+            _ptr(workspace, None, "workspace"), ws_bytes, B, S, N_cap, k, ratio, _stream(stream))
+    return _run("csa_topk", args, prepare)
 
 
 def csa_index_topk_workspace_size(B: int, S: int, N_cap: int, k: int) -> int:
@@ -144,52 +173,60 @@ def csa_index_topk_workspace_size(B: int, S: int, N_cap: int, k: int) -> int:
 
 
 def csa_index_topk(q_idx, w, idx_cache, q_pos, topk_idx, topk_score=None, *, ratio: int, workspace,
-                   relu: bool = True, stream=None):
+                   relu: bool = True, stream=None, prepare: bool = False):
     B, S, Hi, di = q_idx.shape
     N_cap = idx_cache.shape[1]
     k = topk_idx.shape[-1]
     ws_bytes = workspace.numel() * workspace.element_size()
-    rc = load().csa_index_topk(_ptr(q_idx, q_idx.dtype, "q_idx"), _ptr(w, torch.float32, "w"),
-                               _ptr(idx_cache, q_idx.dtype, "idx_cache"), _ptr(q_pos, torch.int32, "q_pos"),
-                               _ptr(topk_idx, torch.int32, "topk_idx"), _ptr(topk_score, torch.float32, "topk_score"),
-                               _ptr(workspace, None, "workspace"), ws_bytes, B, S, Hi, di, N_cap, k, ratio,
-                               0 if relu else CSA_INDEX_NO_RELU, _dtype_code(q_idx), _stream(stream))
-    _check(rc, "csa_index_topk")
+    args = (_ptr(q_idx, q_idx.dtype, "q_idx"), _ptr(w, torch.float32, "w"), _ptr(idx_cache, q_idx.dtype, "idx_cache"),
+            _ptr(q_pos, torch.int32, "q_pos"), _ptr(topk_idx, torch.int32, "topk_idx"),
+            _ptr(topk_score, torch.float32, "topk_score"), _ptr(workspace, None, "workspace"), ws_bytes, B, S, Hi, di,
+            N_cap, k, ratio, 0 if relu else CSA_INDEX_NO_RELU, _dtype_code(q_idx), _stream(stream))
+    return _run("csa_index_topk", args, prepare)
 
 
 def csa_attn_workspace_size(B: int, S: int, H: int, D: int, n_cand: int) -> int:
     return load().csa_attn_workspace_size(B, S, H, D, n_cand)
 
 
+def attn_workspace(B: int, S: int, H: int, D: int, n_cand: int, device) -> Optional[torch.Tensor]:
+    """An attention workspace of the size the library asks for (None when it
+    needs none); its contents need no initialisation."""
+    n = csa_attn_workspace_size(B, S, H, D, n_cand)
+    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+
+
 def csa_sparse_attn(q, cmp_cache, topk_idx, win_kv, win_pos0, sink, q_pos, out, lse=None, *, rope_dim: int,
                     window: int, softmax_scale: Optional[float] = None, rope_base: float = 10000.0, workspace=None,
-                    stream=None):
+                    stream=None, prepare: bool = False):
     B, S, H, D = q.shape
     N_cap = cmp_cache.shape[1]
     k = topk_idx.shape[-1]
     W_cap = win_kv.shape[1]
     scale = softmax_scale if softmax_scale is not None else D ** -0.5
+    if workspace is None:
+        workspace = attn_workspace(B, S, H, D, window + k, q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    rc = load().csa_sparse_attn(_ptr(q, q.dtype, "q"), _ptr(cmp_cache, q.dtype, "cmp_cache"),
-                                _ptr(topk_idx, torch.int32, "topk_idx"), _ptr(win_kv, q.dtype, "win_kv"),
-                                _ptr(win_pos0, torch.int32, "win_pos0"), _ptr(sink, torch.float32, "sink"),
-                                _ptr(q_pos, torch.int32, "q_pos"), _ptr(out, q.dtype, "out"),
-                                _ptr(lse, torch.float32, "lse"), _ptr(workspace, None, "workspace"), ws_bytes, B, S, H,
-                                D, rope_dim, N_cap, k, W_cap, window, scale, rope_base, _dtype_code(q),
-                                _stream(stream))
-    _check(rc, "csa_sparse_attn")
+    args = (_ptr(q, q.dtype, "q"), _ptr(cmp_cache, q.dtype, "cmp_cache"), _ptr(topk_idx, torch.int32, "topk_idx"),
+            _ptr(win_kv, q.dtype, "win_kv"), _ptr(win_pos0, torch.int32, "win_pos0"), _ptr(sink, torch.float32, "sink"),
+            _ptr(q_pos, torch.int32, "q_pos"), _ptr(out, q.dtype, "out"), _ptr(lse, torch.float32, "lse"),
+            _ptr(workspace, None, "workspace"), ws_bytes, B, S, H, D, rope_dim, N_cap, k, W_cap, window, scale,
+            rope_base, _dtype_code(q), _stream(stream))
+    return _run("csa_sparse_attn", args, prepare, keep=(workspace,))
 
 
 def hca_attn(q, cmp_cache, win_kv, win_pos0, sink, q_pos, out, lse=None, *, ratio: int, rope_dim: int, window: int,
-             softmax_scale: Optional[float] = None, rope_base: float = 10000.0, workspace=None, stream=None):
+             softmax_scale: Optional[float] = None, rope_base: float = 10000.0, workspace=None, stream=None,
+             prepare: bool = False):
     B, S, H, D = q.shape
     N_cap = cmp_cache.shape[1]
     W_cap = win_kv.shape[1]
     scale = softmax_scale if softmax_scale is not None else D ** -0.5
+    if workspace is None:
+        workspace = attn_workspace(B, S, H, D, window + N_cap, q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    rc = load().hca_attn(_ptr(q, q.dtype, "q"), _ptr(cmp_cache, q.dtype, "cmp_cache"), _ptr(win_kv, q.dtype, "win_kv"),
-                         _ptr(win_pos0, torch.int32, "win_pos0"), _ptr(sink, torch.float32, "sink"),
-                         _ptr(q_pos, torch.int32, "q_pos"), _ptr(out, q.dtype, "out"), _ptr(lse, torch.float32, "lse"),
-                         _ptr(workspace, None, "workspace"), ws_bytes, B, S, H, D, rope_dim, N_cap, ratio, W_cap,
-                         window, scale, rope_base, _dtype_code(q), _stream(stream))
-    _check(rc, "hca_attn")
+    args = (_ptr(q, q.dtype, "q"), _ptr(cmp_cache, q.dtype, "cmp_cache"), _ptr(win_kv, q.dtype, "win_kv"),
+            _ptr(win_pos0, torch.int32, "win_pos0"), _ptr(sink, torch.float32, "sink"), _ptr(q_pos, torch.int32, "q_pos"),
+            _ptr(out, q.dtype, "out"), _ptr(lse, torch.float32, "lse"), _ptr(workspace, None, "workspace"), ws_bytes,
+            B, S, H, D, rope_dim, N_cap, ratio, W_cap, window, scale, rope_base, _dtype_code(q), _stream(stream))
+    return _run("hca_attn", args, prepare, keep=(workspace,))

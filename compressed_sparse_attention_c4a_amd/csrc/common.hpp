@@ -58,15 +58,18 @@ __device__ __forceinline__ long visible_entries(long t, int ratio, int N_cap) {
 }
 
 // RoPE rotation of interleaved pair i of a rope_dim-wide tail at position pos:
-// theta = pos * base^(-2i/rope_dim).  Angles are formed and reduced in double so
-// that positions up to 2^20 keep full fp32 accuracy in cos/sin.
-__device__ __forceinline__ void rope_cos_sin(double pos, int i, int rope_dim, float base, float* c, float* s) {
-  double inv_freq = pow((double)base, -2.0 * (double)i / (double)rope_dim);
-  double th = pos * inv_freq;
-  double sn, cs;
-  sincos(th, &sn, &cs);
-  *c = (float)cs;
-  *s = (float)sn;
+// theta = pos * base^(-2i/rope_dim), with log2_base = log2(base).  The angle
+// is formed in double and reduced modulo 2*pi by a two-constant Cody-Waite
+// step (|theta| < 2^31 keeps the reduction exact to ~1e-9 rad), so a float
+// sine/cosine of the small remainder keeps full fp32 accuracy for positions
+// up to 2^20 and beyond.
+__device__ __forceinline__ void rope_cos_sin(double pos, int i, int rope_dim, double log2_base, float* c, float* s) {
+  const double inv_freq = exp2(-2.0 * (double)i / (double)rope_dim * log2_base);
+  const double th = pos * inv_freq;
+  const double k = rint(th * 0.15915494309189535);             // th / (2 pi)
+  double r = fma(-k, 6.283185307179586, th);                    // 2 pi, leading part
+  r = fma(-k, 2.4492935982947064e-16, r);                       // 2 pi, trailing part
+  sincosf((float)r, s, c);
 }
 
 // Workgroups are dispatched round-robin over the 8 XCDs (block L -> XCD L % 8),
@@ -135,6 +138,19 @@ __device__ __forceinline__ void lds_barrier() {
   __asm__ volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   __asm__ volatile("" ::: "memory");
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave with DPP moves (no LDS
+// round trips): shifts by 1, 2, 4, 8 inside each 16-lane row, then row 15
+// into rows 1 and 3 and lane 31 into rows 2 and 3.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return x;
 }
 
 __device__ __forceinline__ float wave_sum(float v) {

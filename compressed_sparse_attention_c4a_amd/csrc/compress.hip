@@ -14,14 +14,24 @@
 // softmax in fp32.  Memory-bound and tiny next to the indexer and attention.
 #include "common.hpp"
 
+#include <cmath>
+
 namespace csa {
 
 template <typename T>
 __global__ __launch_bounds__(256) void compress_kernel(const T* __restrict__ kv, const T* __restrict__ sc,
                                                        const float* __restrict__ gamma, T* __restrict__ cache,
                                                        const int32_t* __restrict__ pos0, int L, int d, int rope_dim,
-                                                       int ratio, int overlap, int N_cap, float eps, float base) {
+                                                       int ratio, int overlap, int N_cap, float eps, double log2_base) {
   const int b = blockIdx.y;
+  const int p = threadIdx.x;
+  const bool active = 2 * p < d;
+  // gamma does not depend on the position: its load overlaps the pos0 round trip
+  float gm0 = 0.f, gm1 = 0.f;
+  if (active) {
+    gm0 = gamma[2 * p];
+    gm1 = gamma[2 * p + 1];
+  }
   const long p0 = pos0[b];
   const long g = floor_div(p0, ratio) + blockIdx.x;
   const long first = g * ratio, last = first + ratio - 1;
@@ -34,8 +44,6 @@ __global__ __launch_bounds__(256) void compress_kernel(const T* __restrict__ kv,
   const T* kvb = kv + (size_t)b * L * row_w;
   const T* scb = sc + (size_t)b * L * row_w;
 
-  const int p = threadIdx.x;
-  const bool active = 2 * p < d;
   float y[2] = {0.f, 0.f};
   if (active) {
     // Slots are processed in chunks of 16 whose loads are all issued before
@@ -94,11 +102,11 @@ __global__ __launch_bounds__(256) void compress_kernel(const T* __restrict__ kv,
   const float tot = part[0] + part[1] + part[2] + part[3];
   const float inv = 1.0f / sqrtf(tot / (float)d + eps);
   if (!active) return;
-  float a = y[0] * inv * gamma[2 * p], bb = y[1] * inv * gamma[2 * p + 1];
+  float a = y[0] * inv * gm0, bb = y[1] * inv * gm1;
   const int tail0 = d - rope_dim;
   if (2 * p >= tail0) {
     float cs, sn;
-    rope_cos_sin((double)first, p - tail0 / 2, rope_dim, base, &cs, &sn);
+    rope_cos_sin((double)first, p - tail0 / 2, rope_dim, log2_base, &cs, &sn);
     const float ra = a * cs - bb * sn, rb = a * sn + bb * cs;
     a = ra;
     bb = rb;
@@ -120,10 +128,10 @@ hipError_t launch_compress(const void* kv, const void* sc, const float* gamma, v
   dim3 grid((unsigned)((L + ratio - 1) / ratio + 1), (unsigned)B);
   if (dtype == CSA_F32)
     hipLaunchKernelGGL(compress_kernel<float>, grid, dim3(256), 0, st, (const float*)kv, (const float*)sc, gamma,
-                       (float*)cache, pos0, L, d, rope_dim, ratio, overlap, N_cap, eps, base);
+                       (float*)cache, pos0, L, d, rope_dim, ratio, overlap, N_cap, eps, std::log2((double)base));
   else
     hipLaunchKernelGGL(compress_kernel<bf16>, grid, dim3(256), 0, st, (const bf16*)kv, (const bf16*)sc, gamma,
-                       (bf16*)cache, pos0, L, d, rope_dim, ratio, overlap, N_cap, eps, base);
+                       (bf16*)cache, pos0, L, d, rope_dim, ratio, overlap, N_cap, eps, std::log2((double)base));
   return hipGetLastError();
 }
 

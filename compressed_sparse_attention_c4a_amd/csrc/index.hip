@@ -87,6 +87,21 @@ __global__ __launch_bounds__(256) void index_scores_mfma(const bf16* __restrict_
   float* out = scores + (size_t)qi * N_cap;
   const bf16* Kb = K + (size_t)b * N_cap * 128;
 
+  auto tile_e0 = [&](int i) { return e_chunk + (i * IX_WAVES + wave) * IX_TILE; };
+  auto issue = [&](int i, int buf) {
+    const int e0 = tile_e0(i);
+#pragma unroll
+    for (int j = 0; j < IX_COPIES; ++j) {
+      const int r = 4 * j + (lane >> 4);
+      const int c = (lane & 15) ^ (r & 15);
+      int e = e0 + r;
+      e = e < nv ? e : nv - 1;  // rows past the visible range reload a valid row (masked below)
+      dma16(Kb + (size_t)e * 128 + 8 * c, &lds_k[wave][buf][j * 1024]);
+    }
+  };
+  // the first tile's copy overlaps the q and w loads
+  if (tile_e0(0) < nv) issue(0, 0);
+
   // q_idx -> LDS (swizzled rows), then every wave takes its A fragments.
   {
     const uint4* src = (const uint4*)(q + (size_t)qi * HI * 128);
@@ -107,24 +122,10 @@ __global__ __launch_bounds__(256) void index_scores_mfma(const bf16* __restrict_
     for (int i = 0; i < 4; ++i) wv[mt][i] = w[(size_t)qi * HI + 16 * mt + 4 * g + i];
   }
   const bool relu = !(flags & CSA_INDEX_NO_RELU);
-  // ordinary loads complete before the first tile copy (no compiler wait in
-  // the tile loop can then drain the prefetch)
+  // every ordinary load (q, w) is complete before the tile loop, so no
+  // compiler wait inside it can drain the prefetch
   WAIT_VMCNT(0);
 
-  auto tile_e0 = [&](int i) { return e_chunk + (i * IX_WAVES + wave) * IX_TILE; };
-  auto issue = [&](int i, int buf) {
-    const int e0 = tile_e0(i);
-#pragma unroll
-    for (int j = 0; j < IX_COPIES; ++j) {
-      const int r = 4 * j + (lane >> 4);
-      const int c = (lane & 15) ^ (r & 15);
-      int e = e0 + r;
-      e = e < nv ? e : nv - 1;  // rows past the visible range reload a valid row (masked below)
-      dma16(Kb + (size_t)e * 128 + 8 * c, &lds_k[wave][buf][j * 1024]);
-    }
-  };
-
-  if (tile_e0(0) < nv) issue(0, 0);
   for (int i = 0; i < T; ++i) {
     const int e0 = tile_e0(i);
     if (e0 >= N_cap) break;                   // wave-uniform
@@ -177,10 +178,11 @@ hipError_t launch_index_scores(const void* q, const float* w, const void* K, con
                                hipStream_t st) {
   const int Q = B * S;
   if (dtype == CSA_BF16 && di == 128 && Hi % 16 == 0 && Hi <= 64) {
-    // chunk = 4 waves x T tiles x 32 candidates; aim for ~1024 workgroups (two
-    // resident per CU) without chunks shorter than one tile per wave
+    // chunk = 4 waves x T tiles x 32 candidates; aim for ~512 workgroups (two
+    // resident per CU, all in one round) without chunks shorter than one tile
+    // per wave
     const long cand = (long)Q * N_cap;
-    long per = (cand + 1023) / 1024;
+    long per = (cand + 511) / 512;
     int T = (int)((per + IX_WAVES * IX_TILE - 1) / (IX_WAVES * IX_TILE));
     T = T < 1 ? 1 : T;
     const int chunks = (N_cap + IX_WAVES * T * IX_TILE - 1) / (IX_WAVES * T * IX_TILE);

@@ -5,16 +5,22 @@
 // scores, ties to the lower entry index; outputs are a set padded with -1.
 //
 // One workgroup (16 waves) per query runs an MSD radix select over
-// order-preserving 32-bit keys of the fp32 scores.  Four 8-bit digit passes
-// find K*, the k-th largest key: every wave counts into its own 256-bin LDS
-// histogram (atomics only contend inside a wave), the 16 histograms are
-// summed per bin and a parallel suffix scan over the bins picks the digit
-// where the running count reaches the number of keys still wanted.  One
-// ordered pass then keeps every key > K* and the lowest-index keys == K*:
-// thread t owns a contiguous run of entries, so a single block-wide scan of
-// per-thread counts gives every kept entry its output slot (entry order,
-// deterministic).  Keys live in LDS when a query's scores fit (<= 32768
-// entries); otherwise each pass re-reads the fp32 scores.
+// order-preserving 32-bit keys of the fp32 scores.  Three digit passes (bits
+// 31..21, 20..10, 9..0) find K*, the k-th largest key.  Every pass counts the
+// keys that still match the digits chosen so far into an LDS histogram (2048
+// bins; the top digit holds the sign, the exponent and two mantissa bits, so
+// even the first pass spreads real score distributions over many bins and the
+// LDS atomics rarely collide).  Wave 0 then locates the digit where the count
+// from the top reaches the number of keys still wanted: each lane sums 32
+// bins, a DPP prefix sum over the lanes finds the lane, and that lane walks
+// its bins; meanwhile the other waves clear the second histogram for the next
+// pass, so a pass costs two barriers.  Keys stay in registers (8 or 32 per
+// thread) when a query's scores fit, else every pass re-reads them.  Output:
+// every key > K* and the lowest-index keys == K*; thread t owns entries t,
+// t + 1024, ... and one block-wide scan of per-thread counts gives each kept
+// entry its slot (deterministic).  When more keys equal K* than slots remain
+// (ties across the k-th score), the ties are taken in entry order by a second,
+// contiguous pass.
 #include "common.hpp"
 
 namespace csa {
@@ -26,122 +32,221 @@ __device__ __forceinline__ uint32_t ord_key(float f) {
 
 constexpr int TOPK_THREADS = 1024;
 constexpr int TOPK_WAVES = TOPK_THREADS / 64;
-constexpr int TOPK_LDS_MAX = 32768;
+constexpr int TOPK_BINS = 2048;
 
-// Inclusive prefix sum over the 1024 threads; returns it and sets *total.
-__device__ __forceinline__ int block_inclusive_scan(int v, int* s_w, int* total) {
+// Block-wide exclusive prefix sums of two per-thread counts (1024 threads);
+// totals in *ta, *tb.  Ends with a barrier, so s_w can be reused at once.
+__device__ __forceinline__ void block_excl_scan2(int a, int b, int2* s_w, int* ea, int* eb, int* ta, int* tb) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int u = __shfl_up(v, o, 64);
-    if (lane >= o) v += u;
-  }
-  if (lane == 63) s_w[wid] = v;
+  const int ia = wave_incl_scan(a), ib = wave_incl_scan(b);
+  if (lane == 63) s_w[wid] = make_int2(ia, ib);
   __syncthreads();
-  int before = 0, tot = 0;
+  int pa = 0, pb = 0, sa = 0, sb = 0;
 #pragma unroll
   for (int w = 0; w < TOPK_WAVES; ++w) {
-    const int x = s_w[w];
-    before += (w < wid) ? x : 0;
-    tot += x;
+    const int2 x = s_w[w];
+    pa += (w < wid) ? x.x : 0;
+    pb += (w < wid) ? x.y : 0;
+    sa += x.x;
+    sb += x.y;
   }
-  __syncthreads();  // s_w may be reused by the caller
-  *total = tot;
-  return v + before;
+  __syncthreads();
+  *ea = pa + ia - a;
+  *eb = pb + ib - b;
+  *ta = sa;
+  *tb = sb;
 }
 
-template <bool KEYS_IN_LDS>
+// Wave 0 only: the digit d (of 64 * PER bins, counted from the top) where the
+// number of keys on digits >= d first reaches `remaining`.  Lane l holds the
+// PER bins just below 64*PER - l*PER in registers (vector LDS reads), a DPP
+// prefix sum over the lanes finds the lane, and that lane walks its bins.
+template <int PER>
+__device__ __forceinline__ void find_digit(const uint32_t* h, int lane, uint32_t prefix, int shift, int remaining,
+                                           uint32_t* s_prefix, int* s_remaining) {
+  const int bottom = (63 - lane) * PER;  // lowest digit of this lane's range
+  uint32_t v[PER];
+#pragma unroll
+  for (int i = 0; i < PER / 4; ++i) {
+    const uint4 x = *(const uint4*)&h[bottom + 4 * i];
+    v[4 * i] = x.x;
+    v[4 * i + 1] = x.y;
+    v[4 * i + 2] = x.z;
+    v[4 * i + 3] = x.w;
+  }
+  int c = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) c += (int)v[i];
+  const int incl = wave_incl_scan(c);
+  const uint64_t hit = __builtin_amdgcn_ballot_w64(incl >= remaining);
+  if (lane == (int)__builtin_ctzll(hit)) {  // first lane whose range reaches `remaining`
+    int before = incl - c;
+    int d = bottom;  // reached by the counts; the default only guards the walk
+    bool found = false;
+#pragma unroll
+    for (int i = PER - 1; i >= 0; --i) {
+      const int hc = (int)v[i];
+      if (!found && before + hc >= remaining) {
+        d = bottom + i;
+        found = true;
+      }
+      if (!found) before += hc;
+    }
+    *s_prefix = prefix | ((uint32_t)d << shift);
+    *s_remaining = remaining - before;
+  }
+}
+
+// KPT > 0: each thread holds the keys of entries tid + 1024*j, j < KPT, in
+// registers (requires N_cap <= 1024 * KPT); KPT == 0: keys are re-read.
+template <int KPT>
 __global__ __launch_bounds__(TOPK_THREADS) void topk_radix_kernel(const float* __restrict__ scores,
                                                                   const int32_t* __restrict__ q_pos,
                                                                   int32_t* __restrict__ out_idx,
                                                                   float* __restrict__ out_val, int S, int N_cap,
                                                                   int k, int ratio) {
-  extern __shared__ uint32_t skeys[];
-  __shared__ uint32_t whist[TOPK_WAVES][256];
-  __shared__ int s_w[TOPK_WAVES];
+  __shared__ __attribute__((aligned(16))) uint32_t hist[2][TOPK_BINS];
+  __shared__ int2 s_w[TOPK_WAVES];
   __shared__ uint32_t s_prefix;
   __shared__ int s_remaining;
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int qi = blockIdx.x;
-  const int b = qi / S, s = qi % S;
-  const long t = (long)q_pos[b] + s;
-  const int nv = (int)visible_entries(t, ratio, N_cap);
   const float* sc = scores + (size_t)qi * N_cap;
+  constexpr int KR = KPT > 0 ? KPT : 1;
+  // the score loads do not wait for the position: entries past the visible
+  // range are masked below
+  float kf[KR];
+  if (KPT > 0) {
+#pragma unroll
+    for (int j = 0; j < KR; ++j) {
+      const int e = tid + TOPK_THREADS * j;
+      kf[j] = e < N_cap ? sc[e] : 0.f;
+    }
+  }
+  const int b = qi / S, s = qi % S;
+  const int t = q_pos[b] + s;
+  const int nv = (int)visible_entries(t, ratio, N_cap);
   int32_t* oi = out_idx + (size_t)qi * k;
   float* ov = out_val ? out_val + (size_t)qi * k : nullptr;
   const int kk = k < nv ? k : nv;
-
-  if (KEYS_IN_LDS) {
-    for (int e = tid; e < nv; e += TOPK_THREADS) skeys[e] = ord_key(sc[e]);
-    __syncthreads();
-  }
-  auto key_at = [&](int e) -> uint32_t { return KEYS_IN_LDS ? skeys[e] : ord_key(sc[e]); };
+  uint32_t key[KR];
+#pragma unroll
+  for (int j = 0; j < KR; ++j) key[j] = ord_key(kf[j]);
+  for (int i = tid; i < TOPK_BINS; i += TOPK_THREADS) hist[0][i] = 0;
 
   if (kk == nv) {
     for (int e = tid; e < nv; e += TOPK_THREADS) {  // every visible entry is kept
       oi[e] = e;
       if (ov) ov[e] = sc[e];
     }
-  } else {
+  } else if (kk > 0) {
     uint32_t prefix = 0, mask = 0;
     int remaining = kk;  // keys matching `prefix` still to take
-    for (int shift = 24; shift >= 0; shift -= 8) {
-      for (int i = lane; i < 256; i += 64) whist[wid][i] = 0;
-      __syncthreads();
-      for (int e = tid; e < nv; e += TOPK_THREADS) {
-        const uint32_t key = key_at(e);
-        if ((key & mask) == prefix) atomicAdd(&whist[wid][(key >> shift) & 255u], 1u);
-      }
-      __syncthreads();
-      // thread r < 256 handles digit 255 - r: suffix counts from the top digit
-      int cnt = 0;
-      if (tid < 256) {
+    __syncthreads();     // hist[0] cleared
+#pragma unroll 1
+    for (int pass = 0; pass < 3; ++pass) {
+      const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+      const uint32_t nb = pass == 2 ? 1024u : 2048u;
+      uint32_t* h = hist[pass & 1];
+      if (KPT > 0) {
 #pragma unroll
-        for (int w = 0; w < TOPK_WAVES; ++w) cnt += (int)whist[w][255 - tid];
+        for (int j = 0; j < KR; ++j) {
+          const int e = tid + TOPK_THREADS * j;
+          if (e < nv && (key[j] & mask) == prefix) atomicAdd(&h[(key[j] >> shift) & (nb - 1)], 1u);
+        }
+      } else {
+        for (int e = tid; e < nv; e += TOPK_THREADS) {
+          const uint32_t kv = ord_key(sc[e]);
+          if ((kv & mask) == prefix) atomicAdd(&h[(kv >> shift) & (nb - 1)], 1u);
+        }
       }
-      int tot;
-      const int incl = block_inclusive_scan(tid < 256 ? cnt : 0, s_w, &tot);
-      if (tid < 256 && incl >= remaining && incl - cnt < remaining) {  // exactly one digit
-        s_prefix = prefix | ((uint32_t)(255 - tid) << shift);
-        s_remaining = remaining - (incl - cnt);
+      __syncthreads();  // histogram complete
+      if (wid == 0) {
+        if (nb == 2048)
+          find_digit<32>(h, lane, prefix, shift, remaining, &s_prefix, &s_remaining);
+        else
+          find_digit<16>(h, lane, prefix, shift, remaining, &s_prefix, &s_remaining);
+      } else {
+        uint32_t* hn = hist[(pass + 1) & 1];
+        for (int i = tid - 64; i < TOPK_BINS; i += TOPK_THREADS - 64) hn[i] = 0;
       }
-      __syncthreads();
+      __syncthreads();  // digit chosen; next histogram cleared
       prefix = s_prefix;
       remaining = s_remaining;
-      mask |= 0xFFu << shift;
+      mask |= (nb - 1) << shift;
     }
-    // prefix == K*.  Keys > K* all stay; of the keys == K*, the `remaining`
-    // lowest-index ones stay.  Thread tid owns entries [e0, e1).
-    const int per = (nv + TOPK_THREADS - 1) / TOPK_THREADS;
-    const int e0 = min(nv, tid * per), e1 = min(nv, e0 + per);
+    // prefix == K*.  Keys > K* all stay (n_gt of them); of the keys == K*,
+    // the `remaining` lowest-index ones stay.
     int ngt = 0, neq = 0;
-    for (int e = e0; e < e1; ++e) {
-      const uint32_t key = key_at(e);
-      ngt += key > prefix;
-      neq += key == prefix;
-    }
-    int tot_gt, tot_eq;
-    const int gt_before = block_inclusive_scan(ngt, s_w, &tot_gt) - ngt;
-    const int eq_before = block_inclusive_scan(neq, s_w, &tot_eq) - neq;
-    const int n_gt = kk - remaining;  // == tot_gt
-    int pg = gt_before, pe = eq_before;
-    for (int e = e0; e < e1; ++e) {
-      const uint32_t key = key_at(e);
-      if (key > prefix) {
-        oi[pg] = e;
-        if (ov) ov[pg] = sc[e];
-        ++pg;
-      } else if (key == prefix) {
-        if (pe < remaining) {
-          oi[n_gt + pe] = e;
-          if (ov) ov[n_gt + pe] = sc[e];
-        }
-        ++pe;
+    if (KPT > 0) {
+#pragma unroll
+      for (int j = 0; j < KR; ++j) {
+        const int e = tid + TOPK_THREADS * j;
+        ngt += (e < nv && key[j] > prefix) ? 1 : 0;
+        neq += (e < nv && key[j] == prefix) ? 1 : 0;
+      }
+    } else {
+      for (int e = tid; e < nv; e += TOPK_THREADS) {
+        const uint32_t kv = ord_key(sc[e]);
+        ngt += kv > prefix;
+        neq += kv == prefix;
       }
     }
-    (void)tot_gt;
-    (void)tot_eq;
+    int gt_before, eq_before, tot_gt, tot_eq;
+    block_excl_scan2(ngt, neq, s_w, &gt_before, &eq_before, &tot_gt, &tot_eq);
+    const int n_gt = kk - remaining;  // == tot_gt
+    const bool all_ties = tot_eq == remaining;
+    int pg = gt_before, pe = n_gt + eq_before;
+    if (KPT > 0) {
+#pragma unroll
+      for (int j = 0; j < KR; ++j) {
+        const int e = tid + TOPK_THREADS * j;
+        if (e < nv) {
+          if (key[j] > prefix) {
+            oi[pg] = e;
+            if (ov) ov[pg] = kf[j];
+            ++pg;
+          } else if (all_ties && key[j] == prefix) {
+            oi[pe] = e;
+            if (ov) ov[pe] = kf[j];
+            ++pe;
+          }
+        }
+      }
+    } else {
+      for (int e = tid; e < nv; e += TOPK_THREADS) {
+        const float f = sc[e];
+        const uint32_t kv = ord_key(f);
+        if (kv > prefix) {
+          oi[pg] = e;
+          if (ov) ov[pg] = f;
+          ++pg;
+        } else if (all_ties && kv == prefix) {
+          oi[pe] = e;
+          if (ov) ov[pe] = f;
+          ++pe;
+        }
+      }
+    }
+    if (!all_ties) {
+      // ties straddle the k-th score: the lowest-index `remaining` of them, in
+      // entry order (thread tid owns the contiguous run [e0, e1))
+      const int per = (nv + TOPK_THREADS - 1) / TOPK_THREADS;
+      const int e0 = min(nv, tid * per), e1 = min(nv, e0 + per);
+      int cnt = 0;
+      for (int e = e0; e < e1; ++e) cnt += ord_key(sc[e]) == prefix;
+      int q, unused0, unused1, unused2;
+      block_excl_scan2(cnt, 0, s_w, &q, &unused0, &unused1, &unused2);
+      for (int e = e0; e < e1 && q < remaining; ++e) {
+        const float f = sc[e];
+        if (ord_key(f) == prefix) {
+          oi[n_gt + q] = e;
+          if (ov) ov[n_gt + q] = f;
+          ++q;
+        }
+      }
+    }
   }
   for (int j = kk + tid; j < k; j += TOPK_THREADS) {
     oi[j] = -1;
@@ -159,12 +264,15 @@ size_t topk_workspace_size(int, int, int, int) { return 0; }
 hipError_t launch_topk(const float* scores, const int32_t* q_pos, int32_t* idx, float* val, void*, int B, int S,
                        int N_cap, int k, int ratio, hipStream_t st) {
   const unsigned blocks = (unsigned)(B * S);
-  if (N_cap <= TOPK_LDS_MAX)
-    hipLaunchKernelGGL(topk_radix_kernel<true>, dim3(blocks), dim3(TOPK_THREADS), (size_t)N_cap * 4, st, scores,
-                       q_pos, idx, val, S, N_cap, k, ratio);
+  if (N_cap <= 8 * TOPK_THREADS)
+    hipLaunchKernelGGL(topk_radix_kernel<8>, dim3(blocks), dim3(TOPK_THREADS), 0, st, scores, q_pos, idx, val, S,
+                       N_cap, k, ratio);
+  else if (N_cap <= 32 * TOPK_THREADS)
+    hipLaunchKernelGGL(topk_radix_kernel<32>, dim3(blocks), dim3(TOPK_THREADS), 0, st, scores, q_pos, idx, val, S,
+                       N_cap, k, ratio);
   else
-    hipLaunchKernelGGL(topk_radix_kernel<false>, dim3(blocks), dim3(TOPK_THREADS), 0, st, scores, q_pos, idx, val,
-                       S, N_cap, k, ratio);
+    hipLaunchKernelGGL(topk_radix_kernel<0>, dim3(blocks), dim3(TOPK_THREADS), 0, st, scores, q_pos, idx, val, S,
+                       N_cap, k, ratio);
   return hipGetLastError();
 }
 

@@ -45,34 +45,38 @@ class Step:
             self.topk_idx = torch.empty((sh.B, sh.S, sh.k), dtype=torch.int32, device=device)
             ws = K.csa_index_topk_workspace_size(sh.B, sh.S, sh.N_cap, sh.k)
             self.idx_ws = torch.empty(max(ws, 1), dtype=torch.uint8, device=device)
-            aws = K.csa_attn_workspace_size(sh.B, sh.S, sh.H, sh.D, sh.window + sh.k)
+            n_cand = sh.window + sh.k
         else:
-            aws = K.csa_attn_workspace_size(sh.B, sh.S, sh.H, sh.D, sh.window + sh.N_cap)
-        self.attn_ws = torch.empty(max(aws, 1), dtype=torch.uint8, device=device) if aws else None
+            n_cand = sh.window + sh.N_cap
+        self.attn_ws = K.attn_workspace(sh.B, sh.S, sh.H, sh.D, n_cand, device)
 
-    def calls(self, dev: dict, stream=None):
-        """The pass as a list of (name, thunk), in launch order."""
+    def calls(self, dev: dict, stream=None, prepare: bool = False):
+        """The pass as a list of (name, thunk), in launch order.  With
+        prepare=True the thunks are binding.Prepared calls: their arguments
+        are marshalled once and every call re-issues the same launches."""
         sh = self.sh
-        c = [("compress", lambda: K.csa_compress(dev["kv_state"], dev["score_state"], dev["gamma"], dev["cmp_cache"],
-                                                 dev["state_pos0"], ratio=sh.ratio, overlap=sh.overlap,
-                                                 rope_dim=sh.rope, stream=stream))]
+        P = dict(stream=stream, prepare=True)
+
+        def thunk(fn, *a, **kw):
+            if prepare:
+                return fn(*a, **kw, **P)
+            return lambda: fn(*a, **kw, stream=stream)
+
+        c = [("compress", thunk(K.csa_compress, dev["kv_state"], dev["score_state"], dev["gamma"], dev["cmp_cache"],
+                                dev["state_pos0"], ratio=sh.ratio, overlap=sh.overlap, rope_dim=sh.rope))]
         if sh.indexer:
-            c.append(("compress_idx", lambda: K.csa_compress(dev["idx_kv_state"], dev["idx_score_state"],
-                                                             dev["idx_gamma"], dev["idx_cache"], dev["state_pos0"],
-                                                             ratio=sh.ratio, overlap=True, rope_dim=sh.idx_rope,
-                                                             stream=stream)))
-            c.append(("index_topk", lambda: K.csa_index_topk(dev["q_idx"], dev["w"], dev["idx_cache"], dev["q_pos"],
-                                                             self.topk_idx, ratio=sh.ratio, workspace=self.idx_ws,
-                                                             stream=stream)))
-            c.append(("attn", lambda: K.csa_sparse_attn(dev["q"], dev["cmp_cache"], self.topk_idx, dev["win_kv"],
-                                                        dev.get("win_pos0"), dev["sink"], dev["q_pos"], self.out,
-                                                        self.lse, rope_dim=sh.rope, window=sh.window,
-                                                        workspace=self.attn_ws, stream=stream)))
+            c.append(("compress_idx", thunk(K.csa_compress, dev["idx_kv_state"], dev["idx_score_state"],
+                                            dev["idx_gamma"], dev["idx_cache"], dev["state_pos0"], ratio=sh.ratio,
+                                            overlap=True, rope_dim=sh.idx_rope)))
+            c.append(("index_topk", thunk(K.csa_index_topk, dev["q_idx"], dev["w"], dev["idx_cache"], dev["q_pos"],
+                                          self.topk_idx, ratio=sh.ratio, workspace=self.idx_ws)))
+            c.append(("attn", thunk(K.csa_sparse_attn, dev["q"], dev["cmp_cache"], self.topk_idx, dev["win_kv"],
+                                    dev.get("win_pos0"), dev["sink"], dev["q_pos"], self.out, self.lse,
+                                    rope_dim=sh.rope, window=sh.window, workspace=self.attn_ws)))
         else:
-            c.append(("attn", lambda: K.hca_attn(dev["q"], dev["cmp_cache"], dev["win_kv"], dev.get("win_pos0"),
-                                                 dev["sink"], dev["q_pos"], self.out, self.lse, ratio=sh.ratio,
-                                                 rope_dim=sh.rope, window=sh.window, workspace=self.attn_ws,
-                                                 stream=stream)))
+            c.append(("attn", thunk(K.hca_attn, dev["q"], dev["cmp_cache"], dev["win_kv"], dev.get("win_pos0"),
+                                    dev["sink"], dev["q_pos"], self.out, self.lse, ratio=sh.ratio, rope_dim=sh.rope,
+                                    window=sh.window, workspace=self.attn_ws)))
         return c
 
     def run(self, dev: dict, stream=None):
@@ -80,10 +84,11 @@ class Step:
             fn()
         return self.out
 
-    def run_timed(self, dev: dict, stream, events: dict):
+    def run_timed(self, dev: dict, stream, events: dict, calls=None):
         """As run(); calls named in `events` are bracketed by timing events
-        recorded on `stream` (the stream the kernels are launched on)."""
-        for name, fn in self.calls(dev, stream):
+        recorded on `stream` (the stream the kernels are launched on).  `calls`
+        may pass a prepared call list for this dev and stream."""
+        for name, fn in (calls if calls is not None else self.calls(dev, stream)):
             if name in events:
                 a = torch.cuda.Event(enable_timing=True)
                 b = torch.cuda.Event(enable_timing=True)

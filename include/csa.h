@@ -149,8 +149,16 @@ int csa_index_topk(const void* q_idx, const float* w, const void* idx_cache, con
  *   the last rope_dim dims of o_h are rotated back by position t.  The same
  *   row is key and value.
  * Requires: 1 <= window <= W_cap (ring mode), D <= 512, D even, rope_dim
- *   even <= D, k >= 0.  The MFMA path runs for dtype CSA_BF16, D == 512 and
- *   H % 16 == 0; other shapes use a vector-ALU kernel.
+ *   even <= D, k >= 0.  The MFMA path runs for dtype CSA_BF16, D == 512,
+ *   H % 16 == 0, k <= 2048 and window <= 1024; other shapes use a vector-ALU
+ *   kernel.
+ * workspace: csa_attn_workspace_size(B, S, H, D, n_cand) bytes with n_cand =
+ *   window + k (csa_sparse_attn) or window + N_cap (hca_attn); 0 means none
+ *   is needed and workspace may be NULL.  When small batches split each
+ *   query's candidates over several workgroups, the workspace holds their
+ *   partial results until a second kernel on the same stream merges them.
+ *   Its contents need no initialisation; calls that may run at the same
+ *   time need separate workspaces.
  */
 size_t csa_attn_workspace_size(int B, int S, int H, int D, int n_cand);
 int csa_sparse_attn(const void* q, const void* cmp_cache, const int32_t* topk_idx, const void* win_kv,

@@ -1,7 +1,11 @@
 """GPU parity of the attention entry points on shapes that select each
-kernel variant (head groups of 16, 32 and 64 heads per workgroup), in sparse
-(CSA) and dense (HCA) mode, with ring and linear windows, -1 padding anywhere
-in the selection, short contexts and ragged tile tails."""
+kernel variant (16 or 32 heads per workgroup, candidate lists split over 1 to
+16 workgroups, including splits left with no tile), in sparse (CSA) and dense
+(HCA) mode, with ring and linear windows, -1 padding anywhere in the
+selection, short contexts, the largest window and list, and ragged tile
+tails."""
+import zlib
+
 import numpy as np
 import pytest
 import torch
@@ -44,19 +48,30 @@ def _dev(a):
 
 VARIANTS = {
     # name: (B, S, H, N_cap, W_cap, k, q_pos, linear window, window)
-    "hg16_decode": (5, 1, 128, 600, 128, 96, [2399, 1000, 130, 7, 0], False, 128),
-    "hg32_decode": (64, 1, 128, 300, 128, 40, list(range(400, 1040, 10)), False, 128),
-    "hg64_prefill": (1, 160, 128, 200, 160 + 127, 48, [600], True, 128),
-    "hg16_h48": (3, 1, 48, 100, 64, 33, [399, 250, 60], False, 64),
-    "hg32_h96_window_gt_ctx": (100, 1, 96, 64, 128, 20, list(range(0, 200, 2)), False, 128),
+    # 32 heads per workgroup, 2 splits (sparse) / 6 splits, most of them empty (dense)
+    "split_decode_short_ctx": (5, 1, 128, 600, 128, 96, [2399, 1000, 130, 7, 0], False, 128),
+    # 256 (query, head group) items: no split
+    "nosplit_decode": (64, 1, 128, 300, 128, 40, list(range(400, 1040, 10)), False, 128),
+    "prefill_linear_window": (1, 160, 128, 200, 160 + 127, 48, [600], True, 128),
+    # 16 heads per workgroup (H % 32 != 0)
+    "h48_groups_of_16": (3, 1, 48, 100, 64, 33, [399, 250, 60], False, 64),
+    "h96_window_gt_ctx": (100, 1, 96, 64, 128, 20, list(range(0, 200, 2)), False, 128),
+    # largest list and window: 48 tiles in 16 splits of 3
+    "max_list_16_splits": (2, 1, 32, 4096, 1024, 2048, [16383, 9000], False, 1024),
+    # 16 heads, one item, 6 splits
+    "h16_one_item_splits": (1, 1, 16, 2000, 256, 512, [7999], False, 256),
 }
+
+
+def _seed(name):
+    return zlib.crc32(name.encode()) % 1000
 
 
 @pytest.mark.parametrize("name", sorted(VARIANTS))
 @pytest.mark.parametrize("dense", [False, True])
 def test_attention_variants(orc, name, dense):
     B, S, H, N_cap, W_cap, k, q_pos, linear, window = VARIANTS[name]
-    x = _inputs(hash(name) % 1000, B, S, H, N_cap, W_cap, k, q_pos, linear)
+    x = _inputs(_seed(name), B, S, H, N_cap, W_cap, k, q_pos, linear)
     out = torch.empty((B, S, H, 512), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((B, S, H), dtype=torch.float32, device="cuda")
     if dense:
@@ -87,13 +102,15 @@ def test_sparse_with_every_visible_entry_equals_dense():
                       _dev(x["q_pos"]), o1, rope_dim=64, window=128)
     K.hca_attn(_dev(x["q"]), _dev(x["cmp"]), _dev(x["win"]), None, _dev(x["sink"]), _dev(x["q_pos"]), o2, ratio=4,
                rope_dim=64, window=128)
-    # same candidates in the same order: the two kernels must agree bit for bit
+    # same candidates in the same order, and k == N_cap gives both calls the
+    # same split of the list: the two must agree bit for bit
     assert torch.equal(o1, o2)
 
 
-def test_sink_minus_infinity_and_no_rope(orc):
-    B, S, H = 2, 1, 64
-    x = _inputs(9, B, S, H, 50, 128, 16, [199, 150])
+@pytest.mark.parametrize("B,H,N_cap,k,q_pos", [(2, 64, 50, 16, [199, 150]), (1, 32, 2000, 1024, [7000])])
+def test_sink_minus_infinity_and_no_rope(orc, B, H, N_cap, k, q_pos):
+    S = 1
+    x = _inputs(9, B, S, H, N_cap, 128, k, q_pos)
     sink = np.full((H,), -np.inf, dtype=np.float32)
     out = torch.empty((B, S, H, 512), dtype=torch.bfloat16, device="cuda")
     K.csa_sparse_attn(_dev(x["q"]), _dev(x["cmp"]), _dev(x["topk"]), _dev(x["win"]), None, _dev(sink),

@@ -155,9 +155,11 @@ __global__ __launch_bounds__(64) void attn_generic_kernel(AttnArgs a) {
 // unnormalised O, running max and sum to the workspace; attn_merge_kernel
 // (launched next on the same stream) combines them at the common maximum.
 // Rows are XOR-swizzled in LDS: 16-byte granule c of tile row r sits at
-// c ^ swz(r), swz(r) = 2*(r & 7) + ((r >> 3) & 1), which keeps the row reads
-// of QK^T (16 rows per quarter-wave) and the transposed reads of P.V (4 rows
-// x 2 granules per 16 lanes) free of bank conflicts.
+// c ^ swz(r), swz(r) = 2*(r & 3) + ((r >> 2) & 1) + (r & 8).  Any 8
+// consecutive rows from a multiple of 8 get distinct swizzles modulo 8, and
+// any 4 from a multiple of 4 differ in bits 1-2: the row reads of QK^T (8
+// rows of one granule per 128-byte LDS cycle) and the transposed reads of
+// P.V (4 rows x 2 adjacent granules) hit distinct banks.
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
@@ -174,7 +176,7 @@ constexpr int AT_PART = 4 * 8 * 2 * 64 * 4 + 64;  // floats of one partial: O (l
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float AT_SLACK = 16.f;                // log2 headroom of the lazily updated running max
 
-__device__ __forceinline__ int ar_swz(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
+__device__ __forceinline__ int ar_swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1) | (r & 8); }
 
 // Offset (floats) of lane `lane`'s O^T fragment (dim tile dt, head block hb)
 // of wave `wave` inside a partial.
@@ -262,16 +264,20 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(AttnArgs a, int n_hg, in
   const char* winb = (const char*)a.win + (size_t)b * a.W_cap * AT_ROWB;
   const char* cmpb = (const char*)a.cmp + (size_t)b * a.N_cap * AT_ROWB;
 
-  // q fragments (B operand of QK^T): head h0 + 16*hb + n, dims 32*kk + 8*g .. +8
-  bf16x8_t qf[NHB][16];
+  // The HG q rows of the group go once into ring stage 1 (free until tile 1
+  // is copied), swizzled like candidate rows; each wave reads its fragments
+  // from there after the set-up barrier.
+  {
+    const char* qb = (const char*)a.q + ((size_t)qi * a.H + h0) * AT_ROWB;
+#pragma unroll
+    for (int rr = 0; rr < HG / 4; ++rr) {
+      const int r = wave * (HG / 4) + rr;
+      dma16_sbase(qb + (size_t)r * AT_ROWB, 16u * (uint32_t)(lane ^ ar_swz(r)), ring[1] + r * AT_ROWB);
+    }
+  }
   float sinkv[NHB];
 #pragma unroll
-  for (int hb = 0; hb < NHB; ++hb) {
-    const bf16* qrow = (const bf16*)a.q + ((size_t)qi * a.H + h0 + 16 * hb + n) * AT_D + 8 * g;
-#pragma unroll
-    for (int kk = 0; kk < 16; ++kk) qf[hb][kk] = *(const bf16x8_t*)(qrow + 32 * kk);
-    sinkv[hb] = a.sink[h0 + 16 * hb + n];
-  }
+  for (int hb = 0; hb < NHB; ++hb) sinkv[hb] = a.sink[h0 + 16 * hb + n];
 
   // Candidate slots of this split resolved once into LDS: s_rows[jl] >= 0 is
   // compressed entry s_rows[jl], < 0 is window row -1 - s_rows[jl].  Skipped
@@ -298,11 +304,20 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(AttnArgs a, int n_hg, in
     if (lane == 0) s_mask[j0 / AT_TR] = bal;
   }
   if (nsplit == 1) fill_rope_table(rope_cs, t, a.rope_dim, a.log2_base, threadIdx.x, 256);
-  // Every ordinary load is complete before the first tile copy: the compiler
-  // then has no pending load to wait for inside the tile loop (such a wait
-  // would be vmcnt(0) and drain the copies in flight).
+  // Every ordinary load (and the q copy) is complete before the first tile
+  // copy: the compiler then has no pending load to wait for inside the tile
+  // loop (such a wait would be vmcnt(0) and drain the copies in flight).
   WAIT_VMCNT(0);
   __syncthreads();
+  // q fragments (B operand of QK^T): head h0 + 16*hb + n, dims 32*kk + 8*g .. +8
+  bf16x8_t qf[NHB][16];
+#pragma unroll
+  for (int hb = 0; hb < NHB; ++hb) {
+    const uint8_t* qr = ring[1] + (16 * hb + n) * AT_ROWB;
+    const int sw = ar_swz(16 * hb + n);
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) qf[hb][kk] = *(const bf16x8_t*)(qr + 16 * ((4 * kk + g) ^ sw));
+  }
 
   // row ids of this wave's 16 rows of local tile ti (uniform values)
   auto row_ids = [&](int ti, int (&ids)[16]) {
@@ -366,7 +381,7 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(AttnArgs a, int n_hg, in
     if (has_next) row_ids(i + 1, nid);
 
     // 1. logits of this wave's 16 rows for the HG heads (two chains per head
-    //    block); copies 0..7 of tile i+1 interleaved
+    //    block); copies 0..5 of tile i+1 interleaved (6 and 7 go with the softmax)
     f32x4_t S0[NHB], S1[NHB];
 #pragma unroll
     for (int hb = 0; hb < NHB; ++hb) S0[hb] = S1[hb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -377,7 +392,7 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(AttnArgs a, int n_hg, in
       for (int kk = 0; kk < 16; ++kk) rf[kk] = *(const bf16x8_t*)(myrow + 16 * ((4 * kk + g) ^ rsw));
 #pragma unroll
       for (int kk = 0; kk < 16; kk += 2) {
-        if (has_next) copy_row(i + 1, kk / 2, nid[kk / 2]);
+        if (has_next && (kk / 2) % 4 != 3) copy_row(i + 1, (kk / 2) - (kk / 2) / 4, nid[(kk / 2) - (kk / 2) / 4]);
 #pragma unroll
         for (int hb = 0; hb < NHB; ++hb) {
           S0[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rf[kk], qf[hb][kk], S0[hb], 0, 0, 0);
@@ -399,6 +414,7 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(AttnArgs a, int n_hg, in
       up = up || lm[hb] > m_run[hb] + AT_SLACK;
     }
     const bool moved = __builtin_amdgcn_ballot_w64(up) != 0;
+    if (has_next) copy_row(i + 1, 6, nid[6]);
     auto write_p = [&]() {
 #pragma unroll
       for (int hb = 0; hb < NHB; ++hb) {
@@ -415,6 +431,7 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(AttnArgs a, int n_hg, in
       }
     };
     write_p();
+    if (has_next) copy_row(i + 1, 7, nid[7]);
 #pragma unroll
     for (int hb = 0; hb < NHB; ++hb) mbuf[wave][hb][lane] = lm[hb];
     if (lane == 0) fbuf[wave] = moved ? 1u : 0u;
@@ -505,26 +522,21 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(AttnArgs a, int n_hg, in
 }
 
 // Merge of the NS partials of one (query, head group): rescale each to the
-// common maximum, add in split order (deterministic), then finish as above.
-// Block = one wave's share of the partial layout (64 lanes, 128 dims x HG
-// heads); every load is issued before any arithmetic.
+// common maximum, add in split order (deterministic), divide by the sum,
+// de-rotate and store.  Block = 64 lanes covering one wave's share of the
+// partial layout for two of its eight 16-dim tiles (grid: items x 16), so many
+// small blocks keep the partial reads in flight; every load is issued before
+// any arithmetic.
 template <int NHB>
 __global__ __launch_bounds__(64) void attn_merge_kernel(AttnArgs a, int n_hg, int nsplit,
                                                         const float* __restrict__ part) {
-  __shared__ float2 rope_cs[AT_D / 2];
-  const int qh = blockIdx.x >> 2, wave = blockIdx.x & 3;
+  const int qh = blockIdx.x >> 4, wave = (blockIdx.x >> 2) & 3, dt0 = 2 * (blockIdx.x & 3);
   const int qi = qh / n_hg, hgi = qh % n_hg;
   const int b = qi / a.S, s = qi % a.S;
   const int t = a.q_pos[b] + s;
-  const int lane = threadIdx.x, n = lane & 15;
-  const bool rot = wave * 128 + 128 > AT_D - a.rope_dim;  // this slice reaches the RoPE tail
-  if (rot) {
-    fill_rope_table(rope_cs, t, a.rope_dim, a.log2_base, lane, 64);
-    __syncthreads();
-  }
+  const int lane = threadIdx.x, g = lane >> 4, n = lane & 15;
   const float* pq = part + (size_t)qh * nsplit * AT_PART;
-  f32x4_t o[8][NHB];
-  float L[NHB], M[NHB];
+  const int tail0 = AT_D - a.rope_dim;
 #pragma unroll
   for (int hb = 0; hb < NHB; ++hb) {
     const int mi = AT_PART - 64 + (16 * hb + n) * 2;
@@ -532,22 +544,42 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(AttnArgs a, int n_hg, in
     for (int s2 = 0; s2 < nsplit; ++s2) mx = fmaxf(mx, pq[(size_t)s2 * AT_PART + mi]);
     const float mref = (mx == -INFINITY) ? 0.f : mx;
     float l = 0.f;
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) o[dt][hb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    f32x4_t o[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
     for (int s2 = 0; s2 < nsplit; ++s2) {
       const float* ps = pq + (size_t)s2 * AT_PART;
-      f32x4_t v[8];
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) v[dt] = *(const f32x4_t*)(ps + part_off(wave, dt, hb, lane));
+      const f32x4_t v0 = *(const f32x4_t*)(ps + part_off(wave, dt0, hb, lane));
+      const f32x4_t v1 = *(const f32x4_t*)(ps + part_off(wave, dt0 + 1, hb, lane));
       const float fs = __builtin_amdgcn_exp2f(ps[mi] - mref);
       l += ps[mi + 1] * fs;
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) o[dt][hb] += fs * v[dt];
+      o[0] += fs * v0;
+      o[1] += fs * v1;
     }
-    L[hb] = l;
-    M[hb] = mx;
+    const float inv_l = 1.f / l;
+    const int h = hgi * 16 * NHB + 16 * hb + n;
+    bf16* outp = (bf16*)a.out + ((size_t)qi * a.H + h) * AT_D;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int dim = wave * 128 + 16 * (dt0 + j) + 4 * g;
+      float v[4];
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) v[ii] = o[j][ii] * inv_l;
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp) {
+        if (dim + 2 * pp >= tail0) {
+          float cs, sn;
+          rope_cos_sin((double)t, (dim + 2 * pp - tail0) / 2, a.rope_dim, a.log2_base, &cs, &sn);
+          const float x0 = v[2 * pp], x1 = v[2 * pp + 1];
+          v[2 * pp] = x0 * cs + x1 * sn;
+          v[2 * pp + 1] = -x0 * sn + x1 * cs;
+        }
+      }
+      uint2 pk;
+      pk.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
+      pk.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
+      *(uint2*)(outp + dim) = pk;
+    }
+    if (a.lse && wave == 0 && dt0 == 0 && g == 0) a.lse[(size_t)qi * a.H + h] = (mx + log2f(l)) / LOG2E;
   }
-  store_output<NHB>(a, qi, hgi * 16 * NHB, wave, lane, o, L, M, rope_cs);
 }
 
 }  // namespace csa
@@ -599,11 +631,11 @@ hipError_t launch_attn(const void* q, const void* cmp, const int32_t* topk_idx, 
     if (p.nhb == 2) {
       hipLaunchKernelGGL((attn_tile_kernel<2>), dim3(p.total), dim3(256), 0, st, a, p.n_hg, p.nsplit, p.total, part);
       if (p.nsplit > 1)
-        hipLaunchKernelGGL((attn_merge_kernel<2>), dim3(items * 4), dim3(64), 0, st, a, p.n_hg, p.nsplit, part);
+        hipLaunchKernelGGL((attn_merge_kernel<2>), dim3(items * 16), dim3(64), 0, st, a, p.n_hg, p.nsplit, part);
     } else {
       hipLaunchKernelGGL((attn_tile_kernel<1>), dim3(p.total), dim3(256), 0, st, a, p.n_hg, p.nsplit, p.total, part);
       if (p.nsplit > 1)
-        hipLaunchKernelGGL((attn_merge_kernel<1>), dim3(items * 4), dim3(64), 0, st, a, p.n_hg, p.nsplit, part);
+        hipLaunchKernelGGL((attn_merge_kernel<1>), dim3(items * 16), dim3(64), 0, st, a, p.n_hg, p.nsplit, part);
     }
     return hipGetLastError();
   }

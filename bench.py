@@ -104,6 +104,19 @@ def cpu_baseline(inp, seconds: float):
                       f"{sh.name} ({sh.B * sh.S} queries each), {dt:.1f} s wall"}
 
 
+def copy_calibration(nbytes: int, reps: int = 5):
+    """A plain device-to-device copy of known size (nbytes read, nbytes
+    written per launch): what FETCH_SIZE / WRITE_SIZE report for it scales
+    the counters of the hot-path kernels to bytes."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": nbytes, "launches": reps}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -113,7 +126,12 @@ def main():
     ap.add_argument("--rotate", type=int, default=0, help="input copies to rotate (0: enough to defeat the MALL)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="wall time of the CPU oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES bytes (HBM counter calibration) and exit")
     args = ap.parse_args()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1"}))
         sys.exit(2)
@@ -150,20 +168,25 @@ def main():
         else:
             st.run_timed(d, stream, events, pc)
 
-    # warm-up, with per-call events to find the dominant call
-    ev_warm = {c: [] for c in calls}
+    # warm-up, then a probe pass with events around every call to find the
+    # dominant one (the timed region below brackets only that call)
     for i in range(args.warmup):
-        run_one(i, ev_warm)
+        run_one(i)
     torch.cuda.synchronize()
-    avg_warm = {c: np.mean([a.elapsed_time(b) for a, b in ev_warm[c]]) if ev_warm[c] else 0.0 for c in calls}
-    dominant = max(avg_warm, key=avg_warm.get)
+    ev_probe = {c: [] for c in calls}
+    n_probe = max(10, min(args.steps, 50))
+    for i in range(n_probe):
+        run_one(args.warmup + i, ev_probe)
+    torch.cuda.synchronize()
+    avg_probe = {c: float(np.mean([a.elapsed_time(b) for a, b in ev_probe[c]])) for c in calls}
+    dominant = max(avg_probe, key=avg_probe.get)
 
     # timed region: exactly K steps; events only around the dominant call
     dom_events = {dominant: []}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        run_one(args.warmup + i, dom_events)
+        run_one(args.warmup + n_probe + i, dom_events)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     dom_ms = float(np.mean([a.elapsed_time(b) for a, b in dom_events[dominant]]))
@@ -210,7 +233,7 @@ def main():
                    "input_copies_rotated": R},
         "roofline": roof,
         "whole_step": whole,
-        "warmup_call_us": {c: round(v * 1e3, 2) for c, v in avg_warm.items()},
+        "call_us": {c: round(v * 1e3, 2) for c, v in avg_probe.items()},
         "cpu_baseline": cpu,
     }
     print(json.dumps(res))

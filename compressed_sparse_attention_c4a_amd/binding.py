@@ -37,6 +37,8 @@ def load() -> ctypes.CDLL:
         "csa_error_string": ([i32], ctypes.c_char_p),
         "csa_last_error": ([], ctypes.c_char_p),
         "csa_compress": ([vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, f32, i32, vp], i32),
+        "csa_compress_kv_index": ([vp, vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, i32, i32, i32, vp, i32, i32,
+                                   i32, f32, f32, i32, vp], i32),
         "csa_index_scores": ([vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, u32, i32, vp], i32),
         "csa_topk_workspace_size": ([i32, i32, i32, i32], sz),
         "csa_topk": ([vp, vp, vp, vp, vp, sz, i32, i32, i32, i32, i32, vp], i32),
@@ -141,6 +143,25 @@ def csa_compress(kv_state, score_state, gamma, cache, pos0, *, ratio: int, overl
             _ptr(cache, dt, "cache"), _ptr(pos0, torch.int32, "pos0"), B, L, d, rope_dim, ratio, int(overlap),
             cache.shape[1], eps, rope_base, _dtype_code(kv_state), _stream(stream))
     return _run("csa_compress", args, prepare)
+
+
+def csa_compress_kv_index(kv_state, score_state, gamma, cache, idx_kv_state, idx_score_state, idx_gamma, idx_cache,
+                          pos0, *, ratio: int, overlap: bool, rope_dim: int, idx_rope_dim: int, eps: float = 1e-6,
+                          rope_base: float = 10000.0, stream=None, prepare: bool = False):
+    B, L, md = kv_state.shape
+    d, di = cache.shape[-1], idx_cache.shape[-1]
+    if md != (2 if overlap else 1) * d or score_state.shape != kv_state.shape:
+        raise ValueError("state width must be (2 if overlap else 1) * d and kv/score shapes must match")
+    if idx_kv_state.shape != (B, L, 2 * di) or idx_score_state.shape != idx_kv_state.shape:
+        raise ValueError("index states must be [B, L, 2 * di] over the same tokens")
+    dt = kv_state.dtype
+    args = (_ptr(kv_state, dt, "kv_state"), _ptr(score_state, dt, "score_state"), _ptr(gamma, torch.float32, "gamma"),
+            _ptr(cache, dt, "cache"), d, rope_dim, int(overlap), cache.shape[1],
+            _ptr(idx_kv_state, dt, "idx_kv_state"), _ptr(idx_score_state, dt, "idx_score_state"),
+            _ptr(idx_gamma, torch.float32, "idx_gamma"), _ptr(idx_cache, dt, "idx_cache"), di, idx_rope_dim,
+            idx_cache.shape[1], _ptr(pos0, torch.int32, "pos0"), B, L, ratio, eps, rope_base, _dtype_code(kv_state),
+            _stream(stream))
+    return _run("csa_compress_kv_index", args, prepare)
 
 
 def csa_index_scores(q_idx, w, idx_cache, q_pos, scores, *, ratio: int, relu: bool = True, stream=None,

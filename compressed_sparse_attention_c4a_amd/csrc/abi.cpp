@@ -113,8 +113,43 @@ int csa_compress(const void* kv_state, const void* score_state, const float* gam
   REQ(eps >= 0.f, "%s: eps must be >= 0", fn);
   REQ((L + ratio - 1) / ratio + 1 <= 65535 * 1024, "%s: L too large", fn);
   REQ(B <= 65535, "%s: B must be <= 65535", fn);
-  return launched(fn, csa_host::launch_compress(kv_state, score_state, gamma, cache, pos0, B, L, d, rope_dim, ratio,
-                                                overlap, N_cap, eps, rope_base, dtype, (hipStream_t)stream));
+  const csa::CompressJob job{kv_state, score_state, gamma, cache, d, rope_dim, overlap, N_cap};
+  return launched(fn, csa_host::launch_compress(&job, 1, pos0, B, L, ratio, eps, rope_base, dtype,
+                                                (hipStream_t)stream));
+}
+
+int csa_compress_kv_index(const void* kv_state, const void* score_state, const float* gamma, void* cache, int d,
+                          int rope_dim, int overlap, int N_cap, const void* idx_kv_state,
+                          const void* idx_score_state, const float* idx_gamma, void* idx_cache, int di,
+                          int idx_rope_dim, int idx_N_cap, const int32_t* pos0, int B, int L, int ratio, float eps,
+                          float rope_base, int dtype, csa_stream_t stream) {
+  const char* fn = "csa_compress_kv_index";
+  if (int rc = check_dtype(fn, dtype)) return rc;
+  REQ_PTR(kv_state);
+  REQ_PTR(score_state);
+  REQ_PTR(gamma);
+  REQ_PTR(cache);
+  REQ_PTR(idx_kv_state);
+  REQ_PTR(idx_score_state);
+  REQ_PTR(idx_gamma);
+  REQ_PTR(idx_cache);
+  REQ_PTR(pos0);
+  REQ(B >= 1 && L >= 1 && N_cap >= 1 && idx_N_cap >= 1, "%s: B, L, N_cap, idx_N_cap must be >= 1", fn);
+  REQ(d >= 2 && d <= 512 && d % 2 == 0, "%s: d must be even and in [2, 512] (got %d)", fn, d);
+  REQ(di >= 2 && di <= 512 && di % 2 == 0, "%s: di must be even and in [2, 512] (got %d)", fn, di);
+  REQ(rope_dim >= 0 && rope_dim <= d && rope_dim % 2 == 0, "%s: rope_dim must be even and <= d", fn);
+  REQ(idx_rope_dim >= 0 && idx_rope_dim <= di && idx_rope_dim % 2 == 0, "%s: idx_rope_dim must be even and <= di",
+      fn);
+  REQ(ratio >= 1 && ratio <= 4096, "%s: ratio must be in [1, 4096]", fn);
+  REQ(overlap == 0 || overlap == 1, "%s: overlap must be 0 or 1", fn);
+  REQ(eps >= 0.f, "%s: eps must be >= 0", fn);
+  REQ((L + ratio - 1) / ratio + 1 <= 65535 * 1024, "%s: L too large", fn);
+  REQ(B <= 65535, "%s: B must be <= 65535", fn);
+  const csa::CompressJob jobs[2] = {{kv_state, score_state, gamma, cache, d, rope_dim, overlap, N_cap},
+                                    {idx_kv_state, idx_score_state, idx_gamma, idx_cache, di, idx_rope_dim, 1,
+                                     idx_N_cap}};
+  return launched(fn, csa_host::launch_compress(jobs, 2, pos0, B, L, ratio, eps, rope_base, dtype,
+                                                (hipStream_t)stream));
 }
 
 static int check_index(const char* fn, const void* q_idx, const float* w, const void* idx_cache,

@@ -167,11 +167,21 @@ __device__ __forceinline__ float wave_max(float v) {
 
 }  // namespace csa
 
+namespace csa {
+// One compression job (see compress.hip).
+struct CompressJob {
+  const void* kv;
+  const void* sc;
+  const float* gamma;
+  void* cache;
+  int d, rope_dim, overlap, N_cap;
+};
+}  // namespace csa
+
 // Host-side launch helpers implemented per kernel file; called from abi.cpp.
 namespace csa_host {
-hipError_t launch_compress(const void* kv, const void* sc, const float* gamma, void* cache, const int32_t* pos0, int B,
-                           int L, int d, int rope_dim, int ratio, int overlap, int N_cap, float eps, float base,
-                           int dtype, hipStream_t st);
+hipError_t launch_compress(const csa::CompressJob* jobs, int njobs, const int32_t* pos0, int B, int L, int ratio,
+                           float eps, float base, int dtype, hipStream_t st);
 hipError_t launch_index_scores(const void* q, const float* w, const void* K, const int32_t* q_pos, float* scores,
                                int B, int S, int Hi, int di, int N_cap, int ratio, unsigned flags, int dtype,
                                hipStream_t st);

@@ -9,8 +9,8 @@
 // group's first-half channels together with its own group's second-half
 // channels; 3.1: C128A pools its own 128 tokens only.
 //
-// One workgroup per (sequence, candidate group); thread p owns the channel
-// pair (2p, 2p+1), which is also a RoPE pair.  Slots are folded with an online
+// One workgroup per (sequence, candidate group, job); thread p owns the
+// channel pair (2p, 2p+1), which is also a RoPE pair.  Slots are folded with an online
 // softmax in fp32.  Memory-bound and tiny next to the indexer and attention.
 #include "common.hpp"
 
@@ -18,11 +18,17 @@
 
 namespace csa {
 
+// blockIdx.z selects the job (j0 or j1): both compressors of a CSA layer
+// (main KV and index keys) run in one launch.
 template <typename T>
-__global__ __launch_bounds__(256) void compress_kernel(const T* __restrict__ kv, const T* __restrict__ sc,
-                                                       const float* __restrict__ gamma, T* __restrict__ cache,
-                                                       const int32_t* __restrict__ pos0, int L, int d, int rope_dim,
-                                                       int ratio, int overlap, int N_cap, float eps, double log2_base) {
+__global__ __launch_bounds__(256) void compress_kernel(CompressJob j0, CompressJob j1, const int32_t* __restrict__ pos0,
+                                                       int L, int ratio, float eps, double log2_base) {
+  const CompressJob& J = blockIdx.z == 0 ? j0 : j1;
+  const T* __restrict__ kv = (const T*)J.kv;
+  const T* __restrict__ sc = (const T*)J.sc;
+  const float* __restrict__ gamma = J.gamma;
+  T* __restrict__ cache = (T*)J.cache;
+  const int d = J.d, rope_dim = J.rope_dim, overlap = J.overlap, N_cap = J.N_cap;
   const int b = blockIdx.y;
   const int p = threadIdx.x;
   const bool active = 2 * p < d;
@@ -121,17 +127,16 @@ __global__ __launch_bounds__(256) void compress_kernel(const T* __restrict__ kv,
 namespace csa_host {
 using namespace csa;
 
-hipError_t launch_compress(const void* kv, const void* sc, const float* gamma, void* cache, const int32_t* pos0, int B,
-                           int L, int d, int rope_dim, int ratio, int overlap, int N_cap, float eps, float base,
-                           int dtype, hipStream_t st) {
+hipError_t launch_compress(const CompressJob* jobs, int njobs, const int32_t* pos0, int B, int L, int ratio,
+                           float eps, float base, int dtype, hipStream_t st) {
   // Groups that can intersect [pos0, pos0 + L): at most ceil(L / ratio) + 1.
-  dim3 grid((unsigned)((L + ratio - 1) / ratio + 1), (unsigned)B);
+  dim3 grid((unsigned)((L + ratio - 1) / ratio + 1), (unsigned)B, (unsigned)njobs);
+  const CompressJob j1 = njobs > 1 ? jobs[1] : jobs[0];
+  const double l2b = std::log2((double)base);
   if (dtype == CSA_F32)
-    hipLaunchKernelGGL(compress_kernel<float>, grid, dim3(256), 0, st, (const float*)kv, (const float*)sc, gamma,
-                       (float*)cache, pos0, L, d, rope_dim, ratio, overlap, N_cap, eps, std::log2((double)base));
+    hipLaunchKernelGGL(compress_kernel<float>, grid, dim3(256), 0, st, jobs[0], j1, pos0, L, ratio, eps, l2b);
   else
-    hipLaunchKernelGGL(compress_kernel<bf16>, grid, dim3(256), 0, st, (const bf16*)kv, (const bf16*)sc, gamma,
-                       (bf16*)cache, pos0, L, d, rope_dim, ratio, overlap, N_cap, eps, std::log2((double)base));
+    hipLaunchKernelGGL(compress_kernel<bf16>, grid, dim3(256), 0, st, jobs[0], j1, pos0, L, ratio, eps, l2b);
   return hipGetLastError();
 }
 

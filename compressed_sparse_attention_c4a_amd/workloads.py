@@ -192,30 +192,6 @@ def csa_decode_1m(B: int = 8) -> Shape:
                  state_pos0=t - 7, state_len=8, k=1024, seed=4)
 
 
-def algorithmic_bytes_per_query(sh: Shape) -> dict:
-    """Bytes one query must move for each kernel of one pass (what the method
-    reads or writes, not what an implementation happens to re-read)."""
-    e = 2 if sh.dtype == "bf16" else 4
-    t = sh.q_pos
-    nvis = min((t + sh.S) // sh.ratio, sh.N_cap)
-    m = 2 if sh.overlap else 1
-    groups_per_seq = 1 if sh.S == 1 else max(1, sh.S // sh.ratio)
-    comp = 2 * sh.state_len * m * sh.D * e / sh.S + groups_per_seq * sh.D * e / sh.S
-    out = {"compress": comp}
-    nwin = min(sh.window, t + 1)
-    if sh.indexer:
-        out["compress_idx"] = 2 * sh.state_len * 2 * sh.di * e / sh.S + groups_per_seq * sh.di * e / sh.S
-        out["index_score"] = nvis * sh.di * e + sh.Hi * sh.di * e + sh.Hi * 4 + nvis * 4
-        out["topk"] = nvis * 4 + sh.k * 4
-        reads = nwin + min(sh.k, nvis)
-        out["attn"] = reads * sh.D * e + 2 * sh.H * sh.D * e + sh.k * 4
-    else:
-        reads = nwin + nvis
-        out["attn"] = reads * sh.D * e + 2 * sh.H * sh.D * e
-    out["reads"] = reads
-    return out
-
-
 def slice_batch(inp: dict, n: int) -> dict:
     """The first n batch rows of a generated workload (pure slicing)."""
     sh = dataclasses.replace(inp["shape"], B=n)

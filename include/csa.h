@@ -87,6 +87,21 @@ int csa_compress(const void* kv_state, const void* score_state, const float* gam
                  float eps, float rope_base, int dtype, csa_stream_t stream);
 
 /*
+ * csa_compress_kv_index -- both compressors of a CSA layer in one launch: the
+ * main KV cache (as csa_compress with d, rope_dim, overlap, N_cap) and the
+ * index-key cache, which [P5] 2.2 builds with its own C4A compressor
+ * (always overlapping; di, idx_rope_dim, idx_gamma, idx_N_cap).  Both state
+ * buffers cover the same tokens: [B, L, m*d] and [B, L, 2*di] with row r at
+ * absolute token pos0[b] + r.  Results are identical to two csa_compress
+ * calls.  Requires what csa_compress requires, for both jobs.
+ */
+int csa_compress_kv_index(const void* kv_state, const void* score_state, const float* gamma, void* cache, int d,
+                          int rope_dim, int overlap, int N_cap, const void* idx_kv_state,
+                          const void* idx_score_state, const float* idx_gamma, void* idx_cache, int di,
+                          int idx_rope_dim, int idx_N_cap, const int32_t* pos0, int B, int L, int ratio, float eps,
+                          float rope_base, int dtype, csa_stream_t stream);
+
+/*
  * csa_index_scores -- indexer scores, [P1] "少读 KV 之前，Indexer 仍要给历史打分";
  * [P5] 2.2.
  *

@@ -77,6 +77,25 @@ def test_compress_stage(case, orc):
         np.testing.assert_array_equal(raw_np(dev["idx_cache"])[~iw], inp["idx_cache"][~iw])
 
 
+def test_paired_compress_equals_two_calls(case):
+    """csa_compress_kv_index (one launch) writes exactly what two csa_compress
+    calls write, and nothing else."""
+    name, inp, _ = case
+    sh = inp["shape"]
+    if not sh.indexer:
+        pytest.skip("HCA has no index-key compressor")
+    a, b = P.to_device(inp), P.to_device(inp)
+    K.csa_compress(a["kv_state"], a["score_state"], a["gamma"], a["cmp_cache"], a["state_pos0"], ratio=sh.ratio,
+                   overlap=sh.overlap, rope_dim=sh.rope)
+    K.csa_compress(a["idx_kv_state"], a["idx_score_state"], a["idx_gamma"], a["idx_cache"], a["state_pos0"],
+                   ratio=sh.ratio, overlap=True, rope_dim=sh.idx_rope)
+    K.csa_compress_kv_index(b["kv_state"], b["score_state"], b["gamma"], b["cmp_cache"], b["idx_kv_state"],
+                            b["idx_score_state"], b["idx_gamma"], b["idx_cache"], b["state_pos0"], ratio=sh.ratio,
+                            overlap=sh.overlap, rope_dim=sh.rope, idx_rope_dim=sh.idx_rope)
+    np.testing.assert_array_equal(raw_np(a["cmp_cache"]), raw_np(b["cmp_cache"]))
+    np.testing.assert_array_equal(raw_np(a["idx_cache"]), raw_np(b["idx_cache"]))
+
+
 def test_index_score_stage(case, orc):
     name, inp, ref = case
     sh = inp["shape"]

@@ -537,22 +537,49 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(AttnArgs a, int n_hg, in
   const int lane = threadIdx.x, g = lane >> 4, n = lane & 15;
   const float* pq = part + (size_t)qh * nsplit * AT_PART;
   const int tail0 = AT_D - a.rope_dim;
+  // all partial loads first (one memory round trip for up to AT_MQ splits)
+  constexpr int AT_MQ = 4;
+  f32x4_t v[AT_MQ][NHB][2];
+  float2 ml[AT_MQ][NHB];
+  const int nq = nsplit < AT_MQ ? nsplit : AT_MQ;
+#pragma unroll
+  for (int s2 = 0; s2 < AT_MQ; ++s2) {
+    if (s2 < nq) {
+      const float* ps = pq + (size_t)s2 * AT_PART;
+#pragma unroll
+      for (int hb = 0; hb < NHB; ++hb) {
+        v[s2][hb][0] = *(const f32x4_t*)(ps + part_off(wave, dt0, hb, lane));
+        v[s2][hb][1] = *(const f32x4_t*)(ps + part_off(wave, dt0 + 1, hb, lane));
+        ml[s2][hb] = *(const float2*)(ps + AT_PART - 64 + (16 * hb + n) * 2);
+      }
+    }
+  }
 #pragma unroll
   for (int hb = 0; hb < NHB; ++hb) {
     const int mi = AT_PART - 64 + (16 * hb + n) * 2;
     float mx = -INFINITY;
-    for (int s2 = 0; s2 < nsplit; ++s2) mx = fmaxf(mx, pq[(size_t)s2 * AT_PART + mi]);
+#pragma unroll
+    for (int s2 = 0; s2 < AT_MQ; ++s2)
+      if (s2 < nq) mx = fmaxf(mx, ml[s2][hb].x);
+    for (int s2 = AT_MQ; s2 < nsplit; ++s2) mx = fmaxf(mx, pq[(size_t)s2 * AT_PART + mi]);
     const float mref = (mx == -INFINITY) ? 0.f : mx;
     float l = 0.f;
     f32x4_t o[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
-    for (int s2 = 0; s2 < nsplit; ++s2) {
+#pragma unroll
+    for (int s2 = 0; s2 < AT_MQ; ++s2) {
+      if (s2 < nq) {
+        const float fs = __builtin_amdgcn_exp2f(ml[s2][hb].x - mref);
+        l += ml[s2][hb].y * fs;
+        o[0] += fs * v[s2][hb][0];
+        o[1] += fs * v[s2][hb][1];
+      }
+    }
+    for (int s2 = AT_MQ; s2 < nsplit; ++s2) {
       const float* ps = pq + (size_t)s2 * AT_PART;
-      const f32x4_t v0 = *(const f32x4_t*)(ps + part_off(wave, dt0, hb, lane));
-      const f32x4_t v1 = *(const f32x4_t*)(ps + part_off(wave, dt0 + 1, hb, lane));
       const float fs = __builtin_amdgcn_exp2f(ps[mi] - mref);
       l += ps[mi + 1] * fs;
-      o[0] += fs * v0;
-      o[1] += fs * v1;
+      o[0] += fs * *(const f32x4_t*)(ps + part_off(wave, dt0, hb, lane));
+      o[1] += fs * *(const f32x4_t*)(ps + part_off(wave, dt0 + 1, hb, lane));
     }
     const float inv_l = 1.f / l;
     const int h = hgi * 16 * NHB + 16 * hb + n;

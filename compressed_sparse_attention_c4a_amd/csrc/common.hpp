@@ -153,6 +153,17 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
   return x;
 }
 
+// Sum of x over the four 16-lane rows of a wave (lanes n, n+16, n+32, n+48),
+// returned in every lane: two gfx950 permlane swaps, no LDS round trip.
+__device__ __forceinline__ float row_sum4(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);  // rows 0<->1, 2<->3
+  const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const uint32_t uy = __float_as_uint(y);
+  const auto b = __builtin_amdgcn_permlane32_swap(uy, uy, false, false);  // halves
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);

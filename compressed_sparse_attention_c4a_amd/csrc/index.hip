@@ -46,25 +46,42 @@ __global__ __launch_bounds__(256) void index_scores_generic(const T* __restrict_
 // MFMA kernel (bf16, di == 128, Hi == 16*MT).  HBM-bound streaming of the
 // index cache: every candidate row (256 B) is read once per query.
 //
-// Workgroup = 4 waves, one query, a chunk of 4*T tiles of 32 candidates
-// (tiles interleaved across the waves so the group streams contiguous rows).
-// Per wave and tile: 8 direct global->LDS copies (1 KiB each, 4 rows) into a
-// private double buffer, tile i+1 in flight while tile i is scored; 80 KiB of
-// LDS lets two workgroups share a CU.  Scores: v_mfma_f32_16x16x32_bf16 with
-// A = q_idx (M = 16 heads, K = 32 dims, kept in VGPRs for the whole kernel)
-// and B = k^T from LDS (N = 16 candidates); C lane l holds heads 4*(l/16)+i
-// of candidate l%16, so the ReLU * w head reduction is in-lane over 4*MT
-// values plus two cross-lane steps.  LDS rows are XOR-swizzled (16-byte
-// granule c of row r sits at c ^ (r & 15)) so the 16 rows a quarter-wave
-// reads fall in distinct banks.
+// Workgroup = 4 waves (one per CU: ~256 workgroups), one query, a chunk of
+// 4*T tiles of 32 candidates (tiles interleaved across the waves so the group
+// streams contiguous rows).  Per wave and tile: 8 direct global->LDS copies
+// (1 KiB each, 4 rows) into a private ring of IX_NB tiles, IX_NB-1 tiles in
+// flight while one is scored.  Scores: v_mfma_f32_16x16x32_bf16 with A =
+// q_idx (M = 16 heads, K = 32 dims, kept in VGPRs for the whole kernel) and
+// B = k^T from LDS (N = 16 candidates); C lane l holds heads 4*(l/16)+i of
+// candidate l%16, so the ReLU * w head reduction is in-lane over 4*MT values
+// plus two cross-lane steps.  LDS rows are XOR-swizzled (16-byte granule c of
+// row r sits at c ^ (r & 15)) so the rows a quarter-wave reads fall in
+// distinct banks.
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int IX_TILE = 32;           // candidates per wave tile
 constexpr int IX_WAVES = 4;
+constexpr int IX_NB = 4;              // tiles per wave ring
 constexpr int IX_ROW = 256;           // bytes per index row (128 bf16)
 constexpr int IX_TILE_BYTES = IX_TILE * IX_ROW;
 constexpr int IX_COPIES = IX_TILE_BYTES / 1024;  // 1 KiB copies per tile and wave
+
+// s_waitcnt vmcnt(n) for a run-time n in [0, 31] (the count is an immediate).
+__device__ __forceinline__ void wait_vmcnt_dyn(int n) {
+  switch (n) {
+#define IX_W(k) \
+  case k:       \
+    WAIT_VMCNT(k); \
+    break;
+    IX_W(0) IX_W(1) IX_W(2) IX_W(3) IX_W(4) IX_W(5) IX_W(6) IX_W(7) IX_W(8) IX_W(9) IX_W(10) IX_W(11) IX_W(12)
+    IX_W(13) IX_W(14) IX_W(15) IX_W(16) IX_W(17) IX_W(18) IX_W(19) IX_W(20) IX_W(21) IX_W(22) IX_W(23) IX_W(24)
+    IX_W(25) IX_W(26) IX_W(27) IX_W(28) IX_W(29) IX_W(30)
+#undef IX_W
+    default:
+      WAIT_VMCNT(0);
+  }
+}
 
 template <int MT>
 __global__ __launch_bounds__(256) void index_scores_mfma(const bf16* __restrict__ q, const float* __restrict__ w,
@@ -74,7 +91,7 @@ __global__ __launch_bounds__(256) void index_scores_mfma(const bf16* __restrict_
                                                          unsigned flags, int T, int chunks) {
   constexpr int HI = 16 * MT;
   __shared__ __attribute__((aligned(16))) uint8_t lds_q[HI * IX_ROW];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_k[IX_WAVES][2][IX_TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_k[IX_WAVES][IX_NB][IX_TILE_BYTES];
 
   const int qi = blockIdx.x / chunks, chunk = blockIdx.x % chunks;
   const int b = qi / S, s = qi % S;
@@ -88,7 +105,13 @@ __global__ __launch_bounds__(256) void index_scores_mfma(const bf16* __restrict_
   const bf16* Kb = K + (size_t)b * N_cap * 128;
 
   auto tile_e0 = [&](int i) { return e_chunk + (i * IX_WAVES + wave) * IX_TILE; };
-  auto issue = [&](int i, int buf) {
+  // tiles of this wave that hold visible candidates: i < nt
+  int nt = 0;
+  {
+    const int first = tile_e0(0);
+    if (first < nv) nt = min(T, (nv - first + IX_WAVES * IX_TILE - 1) / (IX_WAVES * IX_TILE));
+  }
+  auto issue = [&](int i) {
     const int e0 = tile_e0(i);
 #pragma unroll
     for (int j = 0; j < IX_COPIES; ++j) {
@@ -96,59 +119,54 @@ __global__ __launch_bounds__(256) void index_scores_mfma(const bf16* __restrict_
       const int c = (lane & 15) ^ (r & 15);
       int e = e0 + r;
       e = e < nv ? e : nv - 1;  // rows past the visible range reload a valid row (masked below)
-      dma16(Kb + (size_t)e * 128 + 8 * c, &lds_k[wave][buf][j * 1024]);
+      dma16(Kb + (size_t)e * 128 + 8 * c, &lds_k[wave][i % IX_NB][j * 1024]);
     }
   };
-  // the first tile's copy overlaps the q and w loads
-  if (tile_e0(0) < nv) issue(0, 0);
-
-  // q_idx -> LDS (swizzled rows), then every wave takes its A fragments.
-  {
-    const uint4* src = (const uint4*)(q + (size_t)qi * HI * 128);
-    for (int G = threadIdx.x; G < HI * 16; G += 256) {
-      const int h = G >> 4, c = G & 15;
-      *(uint4*)(lds_q + h * IX_ROW + 16 * (c ^ (h & 15))) = src[G];
-    }
-  }
-  __syncthreads();
-  bf16x8_t afr[MT][4];
+  // Set-up in one memory round trip: w into registers, q_idx (swizzled rows)
+  // and the first IX_NB-1 tiles into LDS by direct copies, then one wait.
   float wv[MT][4];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wv[mt][i] = w[(size_t)qi * HI + 16 * mt + 4 * g + i];
+  {
+    const bf16* qb = q + (size_t)qi * HI * 128;
+    for (int j = wave; j < HI / 4; j += IX_WAVES) {  // 1 KiB = 4 q rows per copy
+      const int r = 4 * j + (lane >> 4);
+      const int c = (lane & 15) ^ (r & 15);
+      dma16(qb + (size_t)r * 128 + 8 * c, lds_q + j * 1024);
+    }
+  }
+  for (int i = 0; i < IX_NB - 1 && i < nt; ++i) issue(i);
+  WAIT_VMCNT(0);
+  __syncthreads();
+  bf16x8_t afr[MT][4];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
       afr[mt][kk] = *(const bf16x8_t*)(lds_q + (16 * mt + n) * IX_ROW + 16 * ((4 * kk + g) ^ n));
-#pragma unroll
-    for (int i = 0; i < 4; ++i) wv[mt][i] = w[(size_t)qi * HI + 16 * mt + 4 * g + i];
-  }
   const bool relu = !(flags & CSA_INDEX_NO_RELU);
-  // every ordinary load (q, w) is complete before the tile loop, so no
-  // compiler wait inside it can drain the prefetch
-  WAIT_VMCNT(0);
 
   for (int i = 0; i < T; ++i) {
     const int e0 = tile_e0(i);
-    if (e0 >= N_cap) break;                   // wave-uniform
-    const bool live = e0 < nv;
-    const bool next_live = (i + 1 < T) && tile_e0(i + 1) < nv;
-    if (next_live) issue(i + 1, (i + 1) & 1);
-    // everything older than the just-issued copies is done: tile i and the
-    // previous tile's score store
-    if (next_live)
-      WAIT_VMCNT(IX_COPIES);
-    else
-      WAIT_VMCNT(0);
+    if (e0 >= N_cap) break;  // wave-uniform
     float mine = -INFINITY;
-    if (live) {
-      const uint8_t* kt = lds_k[wave][i & 1];
+    if (i < nt) {
+      if (i + IX_NB - 1 < nt) issue(i + IX_NB - 1);  // into the slot tile i-1 used
+      // vector-memory operations issued after tile i's copies: later tiles'
+      // copies and the score stores of tiles max(0, i-NB+1) .. i-1
+      const int later = min(nt, i + IX_NB) - i - 1;
+      wait_vmcnt_dyn(later * IX_COPIES + min(i, IX_NB - 1));
+      const uint8_t* kt = lds_k[wave][i % IX_NB];
 #pragma unroll
-      for (int nt = 0; nt < IX_TILE / 16; ++nt) {
+      for (int nt2 = 0; nt2 < IX_TILE / 16; ++nt2) {
         f32x4_t acc[MT];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
-          const bf16x8_t bfr = *(const bf16x8_t*)(kt + (16 * nt + n) * IX_ROW + 16 * ((4 * kk + g) ^ n));
+          const bf16x8_t bfr = *(const bf16x8_t*)(kt + (16 * nt2 + n) * IX_ROW + 16 * ((4 * kk + g) ^ n));
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt)
             acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[mt][kk], bfr, acc[mt], 0, 0, 0);
@@ -158,9 +176,8 @@ __global__ __launch_bounds__(256) void index_scores_mfma(const bf16* __restrict_
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
           for (int ii = 0; ii < 4; ++ii) v += wv[mt][ii] * (relu ? fmaxf(acc[mt][ii], 0.f) : acc[mt][ii]);
-        v += __shfl_xor(v, 16, 64);
-        v += __shfl_xor(v, 32, 64);
-        if (g == nt) mine = v;
+        v = row_sum4(v);
+        if (g == nt2) mine = v;
       }
       if (e0 + lane >= nv) mine = -INFINITY;
     }
@@ -178,11 +195,10 @@ hipError_t launch_index_scores(const void* q, const float* w, const void* K, con
                                hipStream_t st) {
   const int Q = B * S;
   if (dtype == CSA_BF16 && di == 128 && Hi % 16 == 0 && Hi <= 64) {
-    // chunk = 4 waves x T tiles x 32 candidates; aim for ~512 workgroups (two
-    // resident per CU, all in one round) without chunks shorter than one tile
-    // per wave
+    // chunk = 4 waves x T tiles x 32 candidates; aim for ~256 workgroups (one
+    // per CU, all in one round) without chunks shorter than one tile per wave
     const long cand = (long)Q * N_cap;
-    long per = (cand + 511) / 512;
+    long per = (cand + 255) / 256;
     int T = (int)((per + IX_WAVES * IX_TILE - 1) / (IX_WAVES * IX_TILE));
     T = T < 1 ? 1 : T;
     const int chunks = (N_cap + IX_WAVES * T * IX_TILE - 1) / (IX_WAVES * T * IX_TILE);

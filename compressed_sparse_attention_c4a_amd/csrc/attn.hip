@@ -131,24 +131,31 @@ __global__ __launch_bounds__(64) void attn_generic_kernel(AttnArgs a) {
 //
 // Work item = (query, group of HG heads, split of the candidate list); the
 // item -> block map is XCD-aware, so all head groups of one query run under
-// one L2 and the query's gathered rows come from HBM once.  Workgroup = 4
-// waves.  Candidates stream in tiles of 64 rows (64 KiB) through a 2-stage
-// LDS ring filled by direct global->LDS copies: wave w copies rows
-// 16w..16w+15 of a tile, one whole 1 KiB row per instruction (a coalesced
-// stream of full cache lines).  The copies of tile i+1 are spread through the
-// matrix work on tile i, so the memory pipe drains while the waves compute
-// instead of stalling them at issue.  Per tile:
-//   S^T[16 rows x HG heads] = R . Q^T for the wave's own 16 rows over all 512
-//     dims (MFMA 16x16x32, A = rows from LDS, B = q fragments held in VGPRs
-//     for the whole kernel): each row crosses LDS once for all HG heads;
-//   online softmax in the exp2 domain, P (bf16, [head][row]) to LDS;
-//   O^T[128 dims x HG heads] += R^T . P^T for the wave's 128-dim slice over
-//     all 64 rows (A = rows read transposed with ds_read_b64_tr_b16, B = P^T
-//     from LDS): each row crosses LDS a second time, again for all HG heads.
-// The running max is common to all waves and moves lazily: a tile whose
-// logits exceed it by more than 2^SLACK raises a flag and every wave takes a
-// rare exact rescale path.  The sink logit is the initial reference of the
-// running max and adds exp2(0) = 1 to the sum exactly once (split 0).
+// one L2 and the query's gathered rows come from HBM once.  Candidates go in
+// tiles of 64 rows (64 KiB) through a 2-stage LDS ring.  Workgroup = 8 waves,
+// two per SIMD, in two roles:
+//   S waves 0-3: wave w owns rows 16w..16w+15 of every tile and holds the q
+//     fragments of all HG heads in VGPRs.  S^T[16 rows x HG heads] = R . Q^T
+//     over all 512 dims (MFMA 16x16x32, A = rows read from LDS), then the
+//     online softmax in the exp2 domain; P (bf16, [head][row]) goes to LDS.
+//   O waves 4-7: wave 4+v owns the 128-dim slice 128v..128v+127 of O and
+//     copies rows 16v..16v+15 of every tile into the ring (direct
+//     global->LDS copies, one whole 1 KiB row per instruction: a coalesced
+//     stream of full cache lines).  O^T[128 dims x HG heads] += R^T . P^T
+//     over the tile's 64 rows (A = rows read transposed with
+//     ds_read_b64_tr_b16, B = P^T from LDS).
+// Per tile i two barriers: X_i (tile i landed, the other stage free) ->
+// S: logits + softmax of tile i while O: copies of tile i+1 into the other
+// stage -> Y_i (P visible) -> O: P.V of tile i, wait for the copies -> X_i+1.
+// Each row crosses LDS three times (copy in, logits, transposed read), each
+// time for all HG heads; with two waves per SIMD one role's LDS and memory
+// waits overlap the other role's matrix work.
+// The running max is common to all S waves and moves lazily: a tile whose
+// logits exceed it by more than 2^SLACK raises a flag; then the S waves take
+// the exact maximum, rewrite P and publish the rescale factors, which the O
+// waves apply to O before that tile's P.V.  The sink logit is the initial
+// reference of the running max and adds exp2(0) = 1 to the sum exactly once
+// (split 0).
 //
 // Splits: when there are too few (query, head group) items to fill the chip,
 // an item's tiles are divided between NS workgroups, each of which writes its
@@ -179,9 +186,9 @@ constexpr float AT_SLACK = 16.f;                // log2 headroom of the lazily u
 __device__ __forceinline__ int ar_swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1) | (r & 8); }
 
 // Offset (floats) of lane `lane`'s O^T fragment (dim tile dt, head block hb)
-// of wave `wave` inside a partial.
-__device__ __forceinline__ int part_off(int wave, int dt, int hb, int lane) {
-  return (((wave * 8 + dt) * 2 + hb) * 64 + lane) * 4;
+// of dim slice `v` inside a partial.
+__device__ __forceinline__ int part_off(int v, int dt, int hb, int lane) {
+  return (((v * 8 + dt) * 2 + hb) * 64 + lane) * 4;
 }
 
 // De-rotation table of position t: (cos, sin) of the rope_dim / 2 tail pairs.
@@ -194,11 +201,11 @@ __device__ __forceinline__ void fill_rope_table(float2* tab, int t, int rope_dim
   }
 }
 
-// Final output of one wave: lane (g, n) holds O^T[dim 128*wave + 16*dt + 4*g
-// + i][head h0 + 16*hb + n]; divide by the sum, de-rotate the RoPE tail at
+// Final output of one dim slice: lane (g, n) holds O^T[dim 128*v + 16*dt +
+// 4*g + i][head h0 + 16*hb + n]; divide by the sum, de-rotate the RoPE tail at
 // position t, store bf16, and the log-sum-exp of the denominator.
 template <int NHB>
-__device__ __forceinline__ void store_output(const AttnArgs& a, int qi, int h0, int wave, int lane,
+__device__ __forceinline__ void store_output(const AttnArgs& a, int qi, int h0, int v, int lane,
                                              const f32x4_t (&o)[8][NHB], const float (&l)[NHB],
                                              const float (&m)[NHB], const float2* rope_cs) {
   const int g = lane >> 4, n = lane & 15;
@@ -209,36 +216,38 @@ __device__ __forceinline__ void store_output(const AttnArgs& a, int qi, int h0, 
     bf16* outp = (bf16*)a.out + ((size_t)qi * a.H + h0 + 16 * hb + n) * AT_D;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
-      const int dim = wave * 128 + 16 * dt + 4 * g;
-      float v[4];
+      const int dim = v * 128 + 16 * dt + 4 * g;
+      float x[4];
 #pragma unroll
-      for (int ii = 0; ii < 4; ++ii) v[ii] = o[dt][hb][ii] * inv_l;
+      for (int ii = 0; ii < 4; ++ii) x[ii] = o[dt][hb][ii] * inv_l;
 #pragma unroll
       for (int pp = 0; pp < 2; ++pp) {
         if (dim + 2 * pp >= tail0) {
           const float2 cs = rope_cs[(dim + 2 * pp - tail0) / 2];
-          const float x0 = v[2 * pp], x1 = v[2 * pp + 1];
-          v[2 * pp] = x0 * cs.x + x1 * cs.y;
-          v[2 * pp + 1] = -x0 * cs.y + x1 * cs.x;
+          const float x0 = x[2 * pp], x1 = x[2 * pp + 1];
+          x[2 * pp] = x0 * cs.x + x1 * cs.y;
+          x[2 * pp + 1] = -x0 * cs.y + x1 * cs.x;
         }
       }
       uint2 pk;
-      pk.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
-      pk.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
+      pk.x = (uint32_t)f2bf(x[0]) | ((uint32_t)f2bf(x[1]) << 16);
+      pk.y = (uint32_t)f2bf(x[2]) | ((uint32_t)f2bf(x[3]) << 16);
       *(uint2*)(outp + dim) = pk;
     }
-    if (a.lse && wave == 0 && g == 0) a.lse[(size_t)qi * a.H + h0 + 16 * hb + n] = (m[hb] + log2f(l[hb])) / LOG2E;
+    if (a.lse && v == 0 && g == 0) a.lse[(size_t)qi * a.H + h0 + 16 * hb + n] = (m[hb] + log2f(l[hb])) / LOG2E;
   }
 }
 
 template <int NHB>
-__global__ __launch_bounds__(256) void attn_tile_kernel(AttnArgs a, int n_hg, int nsplit, int total_items,
+__global__ __launch_bounds__(512) void attn_tile_kernel(AttnArgs a, int n_hg, int nsplit, int total_items,
                                                         float* __restrict__ part) {
   constexpr int HG = 16 * NHB;
   __shared__ __attribute__((aligned(16))) uint8_t ring[2][AT_TILE_B];
   __shared__ __attribute__((aligned(16))) __bf16 pbuf[HG][AT_PST];
-  __shared__ float mbuf[4][NHB][64];
-  __shared__ float lbuf[4][NHB][64];
+  __shared__ float mbuf[4][NHB][64];   // S waves' tile maxima (rescale path)
+  __shared__ float abuf[NHB][16];      // rescale factors for the O waves
+  __shared__ float lbuf[4][NHB][16];   // S waves' sums, then the running max
+  __shared__ float mfin[NHB][16];
   __shared__ uint32_t fbuf[4];
   __shared__ __attribute__((aligned(16))) int32_t s_rows[AT_LIST];
   __shared__ uint64_t s_mask[AT_LIST / AT_TR];
@@ -250,9 +259,10 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(AttnArgs a, int n_hg, in
   const int b = qi / a.S, s = qi % a.S;
   const int t = a.q_pos[b] + s;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const bool is_s = wave < 4;          // wave-uniform role
+  const int w4 = wave & 3;             // S: row block; O: dim slice and copied rows
   const int lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15;
   const int h0 = hgi * HG;
-  const int d0 = wave * 128;  // P.V dim slice of this wave
   const int nwin = max(0, min(t + 1, a.window));
   const int ncmp = a.dense ? (int)visible_entries(t, a.ratio, a.N_cap) : a.k;
   const int ncand = nwin + ncmp;
@@ -264,20 +274,20 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(AttnArgs a, int n_hg, in
   const char* winb = (const char*)a.win + (size_t)b * a.W_cap * AT_ROWB;
   const char* cmpb = (const char*)a.cmp + (size_t)b * a.N_cap * AT_ROWB;
 
-  // The HG q rows of the group go once into ring stage 1 (free until tile 1
-  // is copied), swizzled like candidate rows; each wave reads its fragments
-  // from there after the set-up barrier.
-  {
+  // S waves: the HG q rows of the group once into ring stage 1 (first
+  // overwritten by the copies of tile 1, after barrier X_0), swizzled like
+  // candidate rows.
+  float sinkv[NHB];
+  if (is_s) {
     const char* qb = (const char*)a.q + ((size_t)qi * a.H + h0) * AT_ROWB;
 #pragma unroll
     for (int rr = 0; rr < HG / 4; ++rr) {
-      const int r = wave * (HG / 4) + rr;
+      const int r = w4 * (HG / 4) + rr;
       dma16_sbase(qb + (size_t)r * AT_ROWB, 16u * (uint32_t)(lane ^ ar_swz(r)), ring[1] + r * AT_ROWB);
     }
-  }
-  float sinkv[NHB];
 #pragma unroll
-  for (int hb = 0; hb < NHB; ++hb) sinkv[hb] = a.sink[h0 + 16 * hb + n];
+    for (int hb = 0; hb < NHB; ++hb) sinkv[hb] = a.sink[h0 + 16 * hb + n];
+  }
 
   // Candidate slots of this split resolved once into LDS: s_rows[jl] >= 0 is
   // compressed entry s_rows[jl], < 0 is window row -1 - s_rows[jl].  Skipped
@@ -285,7 +295,7 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(AttnArgs a, int n_hg, in
   // and have their bit cleared in the per-tile validity mask.  Dense
   // candidates beyond the table are formed on the fly (all valid).
   const int nlist = min(ntiles * AT_TR, AT_LIST);
-  for (int j0 = wave * 64; j0 < nlist; j0 += 256) {
+  for (int j0 = wave * 64; j0 < nlist; j0 += 512) {
     const int j = jb0 + j0 + lane;
     int id = -1;
     bool ok = false;
@@ -303,25 +313,17 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(AttnArgs a, int n_hg, in
     const uint64_t bal = __builtin_amdgcn_ballot_w64(ok);
     if (lane == 0) s_mask[j0 / AT_TR] = bal;
   }
-  if (nsplit == 1) fill_rope_table(rope_cs, t, a.rope_dim, a.log2_base, threadIdx.x, 256);
-  // Every ordinary load (and the q copy) is complete before the first tile
-  // copy: the compiler then has no pending load to wait for inside the tile
-  // loop (such a wait would be vmcnt(0) and drain the copies in flight).
+  if (nsplit == 1) fill_rope_table(rope_cs, t, a.rope_dim, a.log2_base, threadIdx.x, 512);
+  // Every ordinary load (and the q copy) is complete here: the compiler then
+  // has no pending load to wait for inside the tile loop (such a wait would
+  // be vmcnt(0) and drain the copies in flight).
   WAIT_VMCNT(0);
   __syncthreads();
-  // q fragments (B operand of QK^T): head h0 + 16*hb + n, dims 32*kk + 8*g .. +8
-  bf16x8_t qf[NHB][16];
-#pragma unroll
-  for (int hb = 0; hb < NHB; ++hb) {
-    const uint8_t* qr = ring[1] + (16 * hb + n) * AT_ROWB;
-    const int sw = ar_swz(16 * hb + n);
-#pragma unroll
-    for (int kk = 0; kk < 16; ++kk) qf[hb][kk] = *(const bf16x8_t*)(qr + 16 * ((4 * kk + g) ^ sw));
-  }
 
-  // row ids of this wave's 16 rows of local tile ti (uniform values)
+  // O waves: row ids (uniform) of the 16 rows this wave copies of local tile
+  // ti, and the copy of one of them into stage ti & 1.
   auto row_ids = [&](int ti, int (&ids)[16]) {
-    const int jl = ti * AT_TR + 16 * wave;  // first local slot this wave copies
+    const int jl = ti * AT_TR + 16 * w4;  // first local slot this wave copies
     if (jl + 16 <= nlist) {
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
@@ -339,10 +341,15 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(AttnArgs a, int n_hg, in
       }
     }
   };
-  // copy row rr of this wave's share of local tile ti into its stage
-  auto copy_row = [&](int ti, int rr, int id) {
-    const char* row = id >= 0 ? cmpb + (size_t)(uint32_t)id * AT_ROWB : winb + (size_t)(uint32_t)(-1 - id) * AT_ROWB;
-    dma16_sbase(row, 16u * (uint32_t)(lane ^ ar_swz(rr)), ring[ti & 1] + (16 * wave + rr) * AT_ROWB);
+  auto copy_tile = [&](int ti) {
+    int ids[16];
+    row_ids(ti, ids);
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {
+      const int id = ids[rr];
+      const char* row = id >= 0 ? cmpb + (size_t)(uint32_t)id * AT_ROWB : winb + (size_t)(uint32_t)(-1 - id) * AT_ROWB;
+      dma16_sbase(row, 16u * (uint32_t)(lane ^ ar_swz(rr)), ring[ti & 1] + (16 * w4 + rr) * AT_ROWB);
+    }
   };
   auto tile_mask = [&](int ti) -> uint64_t {
     if (ti * AT_TR < nlist) return s_mask[ti];
@@ -350,160 +357,185 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(AttnArgs a, int n_hg, in
     return left >= 64 ? ~0ull : ((1ull << left) - 1ull);
   };
 
-  const float sc2 = a.scale * LOG2E;
-  float m_run[NHB], l_run[NHB];
-#pragma unroll
-  for (int hb = 0; hb < NHB; ++hb) {
-    m_run[hb] = sinkv[hb] * LOG2E;
-    l_run[hb] = (split == 0 && wave == 0 && g == 0 && sinkv[hb] != -INFINITY) ? 1.f : 0.f;
-  }
-  f32x4_t o[8][NHB];
+  float m_run[NHB], l_run[NHB];  // S waves
+  f32x4_t o[8][NHB];             // O waves
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
     for (int hb = 0; hb < NHB; ++hb) o[dt][hb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  const int rsw = ar_swz(n);           // swizzle of this lane's QK row (16*wave + n)
-  const int trow = 8 * g + (n >> 2);   // transposed-read row for k-chunk 0 (add 32c, +4)
-
-  if (ntiles > 0) {
-    int ids[16];
-    row_ids(0, ids);
-#pragma unroll
-    for (int rr = 0; rr < 16; ++rr) copy_row(0, rr, ids[rr]);
-  }
-  for (int i = 0; i < ntiles; ++i) {
-    const uint8_t* tile = ring[i & 1];
-    const bool has_next = i + 1 < ntiles;
-    WAIT_VMCNT(0);   // this wave's copies of tile i have landed
-    lds_barrier();   // ... and every wave's; P.V of tile i-1 is done everywhere
-    int nid[16];
-    if (has_next) row_ids(i + 1, nid);
-
-    // 1. logits of this wave's 16 rows for the HG heads (two chains per head
-    //    block); copies 0..5 of tile i+1 interleaved (6 and 7 go with the softmax)
-    f32x4_t S0[NHB], S1[NHB];
-#pragma unroll
-    for (int hb = 0; hb < NHB; ++hb) S0[hb] = S1[hb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    {
-      const uint8_t* myrow = tile + (16 * wave + n) * AT_ROWB;
-      bf16x8_t rf[16];
-#pragma unroll
-      for (int kk = 0; kk < 16; ++kk) rf[kk] = *(const bf16x8_t*)(myrow + 16 * ((4 * kk + g) ^ rsw));
-#pragma unroll
-      for (int kk = 0; kk < 16; kk += 2) {
-        if (has_next && (kk / 2) % 4 != 3) copy_row(i + 1, (kk / 2) - (kk / 2) / 4, nid[(kk / 2) - (kk / 2) / 4]);
-#pragma unroll
-        for (int hb = 0; hb < NHB; ++hb) {
-          S0[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rf[kk], qf[hb][kk], S0[hb], 0, 0, 0);
-          S1[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rf[kk + 1], qf[hb][kk + 1], S1[hb], 0, 0, 0);
-        }
-      }
-    }
-
-    // 2. P with the current running max; lane (g, n): rows 16w + 4g + ii, heads 16hb + n
-    const uint32_t vb = (uint32_t)(tile_mask(i) >> (16 * wave + 4 * g)) & 0xFu;
-    float sv[NHB][4], pv[NHB][4], lm[NHB];
-    bool up = false;
+  if (is_s) {
+    // ---------------------------------------------------------------- S waves
+    // q fragments (B operand of QK^T): head h0 + 16*hb + n, dims 32*kk + 8*g .. +8
+    bf16x8_t qf[NHB][16];
 #pragma unroll
     for (int hb = 0; hb < NHB; ++hb) {
-      const f32x4_t S = S0[hb] + S1[hb];
+      const uint8_t* qr = ring[1] + (16 * hb + n) * AT_ROWB;
+      const int sw = ar_swz(16 * hb + n);
 #pragma unroll
-      for (int ii = 0; ii < 4; ++ii) sv[hb][ii] = ((vb >> ii) & 1u) ? S[ii] * sc2 : -INFINITY;
-      lm[hb] = fmaxf(fmaxf(sv[hb][0], sv[hb][1]), fmaxf(sv[hb][2], sv[hb][3]));
-      up = up || lm[hb] > m_run[hb] + AT_SLACK;
+      for (int kk = 0; kk < 16; ++kk) qf[hb][kk] = *(const bf16x8_t*)(qr + 16 * ((4 * kk + g) ^ sw));
     }
-    const bool moved = __builtin_amdgcn_ballot_w64(up) != 0;
-    if (has_next) copy_row(i + 1, 6, nid[6]);
-    auto write_p = [&]() {
+    const float sc2 = a.scale * LOG2E;
 #pragma unroll
-      for (int hb = 0; hb < NHB; ++hb) {
-        // m_run is -inf only while every logit so far is masked (sink -inf):
-        // the reference 0 then gives p == 0 instead of NaN
-        const float m_ref = (m_run[hb] == -INFINITY) ? 0.f : m_run[hb];
-        bf16x4_t pk;
+    for (int hb = 0; hb < NHB; ++hb) {
+      m_run[hb] = sinkv[hb] * LOG2E;
+      l_run[hb] = (split == 0 && w4 == 0 && g == 0 && sinkv[hb] != -INFINITY) ? 1.f : 0.f;
+    }
+    const int rsw = ar_swz(n);  // swizzle of this lane's row (16*w4 + n)
+    lds_barrier();              // X_0 (every wave has its q fragments before tile 1 is copied)
+    for (int i = 0; i < ntiles; ++i) {
+      const uint8_t* myrow = ring[i & 1] + (16 * w4 + n) * AT_ROWB;
+      // 1. logits of this wave's 16 rows for the HG heads (two chains per head block)
+      f32x4_t S0[NHB], S1[NHB];
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-          pv[hb][ii] = __builtin_amdgcn_exp2f(sv[hb][ii] - m_ref);
-          pk[ii] = (__bf16)pv[hb][ii];
+      for (int hb = 0; hb < NHB; ++hb) S0[hb] = S1[hb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        bf16x8_t rf[8];
+#pragma unroll
+        for (int k2 = 0; k2 < 8; ++k2) {
+          const int kk = 8 * half + k2;
+          rf[k2] = *(const bf16x8_t*)(myrow + 16 * ((4 * kk + g) ^ rsw));
         }
-        *(bf16x4_t*)&pbuf[16 * hb + n][16 * wave + 4 * g] = pk;
-      }
-    };
-    write_p();
-    if (has_next) copy_row(i + 1, 7, nid[7]);
 #pragma unroll
-    for (int hb = 0; hb < NHB; ++hb) mbuf[wave][hb][lane] = lm[hb];
-    if (lane == 0) fbuf[wave] = moved ? 1u : 0u;
-    lds_barrier();  // P, tile maxima and flags of all waves visible
-    if (fbuf[0] | fbuf[1] | fbuf[2] | fbuf[3]) {
-      // rare: some logit left the running max's headroom -> exact rescale
+        for (int k2 = 0; k2 < 8; k2 += 2) {
+          const int kk = 8 * half + k2;
+#pragma unroll
+          for (int hb = 0; hb < NHB; ++hb) {
+            S0[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rf[k2], qf[hb][kk], S0[hb], 0, 0, 0);
+            S1[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rf[k2 + 1], qf[hb][kk + 1], S1[hb], 0, 0, 0);
+          }
+        }
+      }
+      // 2. P with the current running max; lane (g, n): rows 16w + 4g + ii, heads 16hb + n
+      const uint32_t vb = (uint32_t)(tile_mask(i) >> (16 * w4 + 4 * g)) & 0xFu;
+      float sv[NHB][4], pv[NHB][4], lm[NHB];
+      bool up = false;
 #pragma unroll
       for (int hb = 0; hb < NHB; ++hb) {
-        float mt = -INFINITY;
+        const f32x4_t S = S0[hb] + S1[hb];
 #pragma unroll
-        for (int w2 = 0; w2 < 4; ++w2)
-#pragma unroll
-          for (int g2 = 0; g2 < 4; ++g2) mt = fmaxf(mt, mbuf[w2][hb][16 * g2 + n]);
-        const float m_new = fmaxf(m_run[hb], mt);
-        const float alpha = (m_new == m_run[hb]) ? 1.f : __builtin_amdgcn_exp2f(m_run[hb] - m_new);
-        l_run[hb] *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) o[dt][hb] *= alpha;
-        m_run[hb] = m_new;
+        for (int ii = 0; ii < 4; ++ii) sv[hb][ii] = ((vb >> ii) & 1u) ? S[ii] * sc2 : -INFINITY;
+        lm[hb] = fmaxf(fmaxf(sv[hb][0], sv[hb][1]), fmaxf(sv[hb][2], sv[hb][3]));
+        up = up || lm[hb] > m_run[hb] + AT_SLACK;
       }
+      const bool moved = __builtin_amdgcn_ballot_w64(up) != 0;
+      auto write_p = [&]() {
+#pragma unroll
+        for (int hb = 0; hb < NHB; ++hb) {
+          // m_run is -inf only while every logit so far is masked (sink -inf):
+          // the reference 0 then gives p == 0 instead of NaN
+          const float m_ref = (m_run[hb] == -INFINITY) ? 0.f : m_run[hb];
+          bf16x4_t pk;
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) {
+            pv[hb][ii] = __builtin_amdgcn_exp2f(sv[hb][ii] - m_ref);
+            pk[ii] = (__bf16)pv[hb][ii];
+          }
+          *(bf16x4_t*)&pbuf[16 * hb + n][16 * w4 + 4 * g] = pk;
+        }
+      };
       write_p();
-      lds_barrier();
-    }
 #pragma unroll
-    for (int hb = 0; hb < NHB; ++hb) l_run[hb] += (pv[hb][0] + pv[hb][1]) + (pv[hb][2] + pv[hb][3]);
-
-    // 3. O^T[128 dims x HG heads] += R^T[128 x 64 rows] P^T[64 rows x HG heads];
-    //    copies 8..15 of tile i+1 interleaved
+      for (int hb = 0; hb < NHB; ++hb) mbuf[w4][hb][lane] = lm[hb];
+      if (lane == 0) fbuf[w4] = moved ? 1u : 0u;
+      lds_barrier();  // Y_i: P, tile maxima and flags visible
+      if (fbuf[0] | fbuf[1] | fbuf[2] | fbuf[3]) {
+        // rare: some logit left the running max's headroom -> exact maximum,
+        // P again, and the factor for O published to the O waves
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      bf16x8_t pf[NHB];
+        for (int hb = 0; hb < NHB; ++hb) {
+          float mt = -INFINITY;
 #pragma unroll
-      for (int hb = 0; hb < NHB; ++hb) pf[hb] = *(const bf16x8_t*)&pbuf[16 * hb + n][32 * c + 8 * g];
-      const int ra = 32 * c + trow, rb = ra + 4;
-      const uint8_t* pa = tile + ra * AT_ROWB;
-      const uint8_t* pb = tile + rb * AT_ROWB;
-      const int sa = ar_swz(ra), sb = ar_swz(rb);
-      bf16x4_t lo[8], hi[8];
+          for (int w2 = 0; w2 < 4; ++w2)
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        const int dim = d0 + 16 * dt + 4 * (n & 3);
-        const int gr = dim >> 3, half = (dim >> 2) & 1;
-        lo[dt] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-            (__attribute__((address_space(3))) bf16x4_t*)(pa + 16 * (gr ^ sa) + 8 * half));
-        hi[dt] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-            (__attribute__((address_space(3))) bf16x4_t*)(pb + 16 * (gr ^ sb) + 8 * half));
+            for (int g2 = 0; g2 < 4; ++g2) mt = fmaxf(mt, mbuf[w2][hb][16 * g2 + n]);
+          const float m_new = fmaxf(m_run[hb], mt);
+          const float alpha = (m_new == m_run[hb]) ? 1.f : __builtin_amdgcn_exp2f(m_run[hb] - m_new);
+          l_run[hb] *= alpha;
+          if (w4 == 0 && g == 0) abuf[hb][n] = alpha;
+          m_run[hb] = m_new;
+        }
+        write_p();
+        lds_barrier();  // Y'_i
       }
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        if (has_next && (dt & 1) == 0) copy_row(i + 1, 8 + 4 * c + dt / 2, nid[8 + 4 * c + dt / 2]);
-        const bf16x8_t afr = __builtin_shufflevector(lo[dt], hi[dt], 0, 1, 2, 3, 4, 5, 6, 7);
+      for (int hb = 0; hb < NHB; ++hb) l_run[hb] += (pv[hb][0] + pv[hb][1]) + (pv[hb][2] + pv[hb][3]);
+      if (i + 1 < ntiles) lds_barrier();  // X_i+1
+    }
+    // sums over the lane groups, and the running max, for the O waves
 #pragma unroll
-        for (int hb = 0; hb < NHB; ++hb) o[dt][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, pf[hb], o[dt][hb], 0, 0, 0);
+    for (int hb = 0; hb < NHB; ++hb) {
+      float l = l_run[hb];
+      l += __shfl_xor(l, 16, 64);
+      l += __shfl_xor(l, 32, 64);
+      if (g == 0) lbuf[w4][hb][n] = l;
+      if (w4 == 0 && g == 0) mfin[hb][n] = m_run[hb];
+    }
+  } else {
+    // ---------------------------------------------------------------- O waves
+    const int d0 = w4 * 128;            // P.V dim slice of this wave
+    const int trow = 8 * g + (n >> 2);  // transposed-read row for k-chunk 0 (add 32c, +4)
+    if (ntiles > 0) copy_tile(0);
+    WAIT_VMCNT(0);
+    lds_barrier();  // X_0
+    for (int i = 0; i < ntiles; ++i) {
+      const uint8_t* tile = ring[i & 1];
+      if (i + 1 < ntiles) copy_tile(i + 1);  // into the stage tile i-1 used
+      lds_barrier();  // Y_i
+      if (fbuf[0] | fbuf[1] | fbuf[2] | fbuf[3]) {
+        lds_barrier();  // Y'_i: rescale factors and the new P visible
+#pragma unroll
+        for (int hb = 0; hb < NHB; ++hb) {
+          const float alpha = abuf[hb][n];
+#pragma unroll
+          for (int dt = 0; dt < 8; ++dt) o[dt][hb] *= alpha;
+        }
+      }
+      // O^T[128 dims x HG heads] += R^T[128 x 64 rows] P^T[64 rows x HG heads]
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        bf16x8_t pf[NHB];
+#pragma unroll
+        for (int hb = 0; hb < NHB; ++hb) pf[hb] = *(const bf16x8_t*)&pbuf[16 * hb + n][32 * c + 8 * g];
+        const int ra = 32 * c + trow, rb = ra + 4;
+        const uint8_t* pa = tile + ra * AT_ROWB;
+        const uint8_t* pb = tile + rb * AT_ROWB;
+        const int sa = ar_swz(ra), sb = ar_swz(rb);
+        bf16x4_t lo[8], hi[8];
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+          const int dim = d0 + 16 * dt + 4 * (n & 3);
+          const int gr = dim >> 3, hf = (dim >> 2) & 1;
+          lo[dt] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+              (__attribute__((address_space(3))) bf16x4_t*)(pa + 16 * (gr ^ sa) + 8 * hf));
+          hi[dt] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+              (__attribute__((address_space(3))) bf16x4_t*)(pb + 16 * (gr ^ sb) + 8 * hf));
+        }
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+          const bf16x8_t afr = __builtin_shufflevector(lo[dt], hi[dt], 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+          for (int hb = 0; hb < NHB; ++hb) o[dt][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, pf[hb], o[dt][hb], 0, 0, 0);
+        }
+      }
+      if (i + 1 < ntiles) {
+        WAIT_VMCNT(0);    // this wave's copies of tile i+1 have landed
+        lds_barrier();    // X_i+1
       }
     }
   }
+  __syncthreads();  // S waves' sums and maximum visible
+  if (is_s) return;
 
-  // sum per head over the lane groups and waves
-  float l_tot[NHB];
+  float l_tot[NHB], m_fin[NHB];
 #pragma unroll
   for (int hb = 0; hb < NHB; ++hb) {
-    float l = l_run[hb];
-    l += __shfl_xor(l, 16, 64);
-    l += __shfl_xor(l, 32, 64);
-    lbuf[wave][hb][lane] = l;
+    l_tot[hb] = (lbuf[0][hb][n] + lbuf[1][hb][n]) + (lbuf[2][hb][n] + lbuf[3][hb][n]);
+    m_fin[hb] = mfin[hb][n];
   }
-  __syncthreads();
-#pragma unroll
-  for (int hb = 0; hb < NHB; ++hb) l_tot[hb] = (lbuf[0][hb][n] + lbuf[1][hb][n]) + (lbuf[2][hb][n] + lbuf[3][hb][n]);
-
   if (nsplit == 1) {
-    store_output<NHB>(a, qi, h0, wave, lane, o, l_tot, m_run, rope_cs);
+    store_output<NHB>(a, qi, h0, w4, lane, o, l_tot, m_fin, rope_cs);
     return;
   }
   // partial of this split for attn_merge_kernel
@@ -511,11 +543,11 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(AttnArgs a, int n_hg, in
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-    for (int hb = 0; hb < NHB; ++hb) *(f32x4_t*)(po + part_off(wave, dt, hb, lane)) = o[dt][hb];
-  if (wave == 0 && g == 0) {
+    for (int hb = 0; hb < NHB; ++hb) *(f32x4_t*)(po + part_off(w4, dt, hb, lane)) = o[dt][hb];
+  if (w4 == 0 && g == 0) {
 #pragma unroll
     for (int hb = 0; hb < NHB; ++hb) {
-      po[AT_PART - 64 + (16 * hb + n) * 2] = m_run[hb];
+      po[AT_PART - 64 + (16 * hb + n) * 2] = m_fin[hb];
       po[AT_PART - 64 + (16 * hb + n) * 2 + 1] = l_tot[hb];
     }
   }
@@ -656,11 +688,11 @@ hipError_t launch_attn(const void* q, const void* cmp, const int32_t* topk_idx, 
     float* part = p.nsplit > 1 ? (float*)ws : nullptr;
     const int items = p.total / p.nsplit;
     if (p.nhb == 2) {
-      hipLaunchKernelGGL((attn_tile_kernel<2>), dim3(p.total), dim3(256), 0, st, a, p.n_hg, p.nsplit, p.total, part);
+      hipLaunchKernelGGL((attn_tile_kernel<2>), dim3(p.total), dim3(512), 0, st, a, p.n_hg, p.nsplit, p.total, part);
       if (p.nsplit > 1)
         hipLaunchKernelGGL((attn_merge_kernel<2>), dim3(items * 16), dim3(64), 0, st, a, p.n_hg, p.nsplit, part);
     } else {
-      hipLaunchKernelGGL((attn_tile_kernel<1>), dim3(p.total), dim3(256), 0, st, a, p.n_hg, p.nsplit, p.total, part);
+      hipLaunchKernelGGL((attn_tile_kernel<1>), dim3(p.total), dim3(512), 0, st, a, p.n_hg, p.nsplit, p.total, part);
       if (p.nsplit > 1)
         hipLaunchKernelGGL((attn_merge_kernel<1>), dim3(items * 16), dim3(64), 0, st, a, p.n_hg, p.nsplit, part);
     }

@@ -201,15 +201,40 @@ __device__ __forceinline__ void fill_rope_table(float2* tab, int t, int rope_dim
   }
 }
 
-// Final output of one dim slice: lane (g, n) holds O^T[dim 128*v + 16*dt +
-// 4*g + i][head h0 + 16*hb + n]; divide by the sum, de-rotate the RoPE tail at
-// position t, store bf16, and the log-sum-exp of the denominator.
+// Lane (g, n) of dim slice v holds O^T[dim 128*v + 16*dt + 4*g + i][head
+// h0 + 16*hb + n].  The inverse RoPE of position t is a rotation of each tail
+// pair, linear in O: it is applied to unnormalised partial sums as well.
+template <int NHB>
+__device__ __forceinline__ void derotate(f32x4_t (&o)[8][NHB], int v, int lane, int rope_dim,
+                                         const float2* rope_cs) {
+  const int g = lane >> 4;
+  const int tail0 = AT_D - rope_dim;
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) {
+    const int dim = v * 128 + 16 * dt + 4 * g;
+    if (dim + 4 <= tail0) continue;
+#pragma unroll
+    for (int pp = 0; pp < 2; ++pp) {
+      if (dim + 2 * pp >= tail0) {
+        const float2 cs = rope_cs[(dim + 2 * pp - tail0) / 2];
+#pragma unroll
+        for (int hb = 0; hb < NHB; ++hb) {
+          const float x0 = o[dt][hb][2 * pp], x1 = o[dt][hb][2 * pp + 1];
+          o[dt][hb][2 * pp] = x0 * cs.x + x1 * cs.y;
+          o[dt][hb][2 * pp + 1] = -x0 * cs.y + x1 * cs.x;
+        }
+      }
+    }
+  }
+}
+
+// Final output of one dim slice (already de-rotated): divide by the sum,
+// store bf16, and the log-sum-exp of the denominator.
 template <int NHB>
 __device__ __forceinline__ void store_output(const AttnArgs& a, int qi, int h0, int v, int lane,
                                              const f32x4_t (&o)[8][NHB], const float (&l)[NHB],
-                                             const float (&m)[NHB], const float2* rope_cs) {
+                                             const float (&m)[NHB]) {
   const int g = lane >> 4, n = lane & 15;
-  const int tail0 = AT_D - a.rope_dim;
 #pragma unroll
   for (int hb = 0; hb < NHB; ++hb) {
     const float inv_l = 1.f / l[hb];
@@ -220,15 +245,6 @@ __device__ __forceinline__ void store_output(const AttnArgs& a, int qi, int h0, 
       float x[4];
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) x[ii] = o[dt][hb][ii] * inv_l;
-#pragma unroll
-      for (int pp = 0; pp < 2; ++pp) {
-        if (dim + 2 * pp >= tail0) {
-          const float2 cs = rope_cs[(dim + 2 * pp - tail0) / 2];
-          const float x0 = x[2 * pp], x1 = x[2 * pp + 1];
-          x[2 * pp] = x0 * cs.x + x1 * cs.y;
-          x[2 * pp + 1] = -x0 * cs.y + x1 * cs.x;
-        }
-      }
       uint2 pk;
       pk.x = (uint32_t)f2bf(x[0]) | ((uint32_t)f2bf(x[1]) << 16);
       pk.y = (uint32_t)f2bf(x[2]) | ((uint32_t)f2bf(x[3]) << 16);
@@ -313,7 +329,7 @@ __global__ __launch_bounds__(512) void attn_tile_kernel(AttnArgs a, int n_hg, in
     const uint64_t bal = __builtin_amdgcn_ballot_w64(ok);
     if (lane == 0) s_mask[j0 / AT_TR] = bal;
   }
-  if (nsplit == 1) fill_rope_table(rope_cs, t, a.rope_dim, a.log2_base, threadIdx.x, 512);
+  fill_rope_table(rope_cs, t, a.rope_dim, a.log2_base, threadIdx.x, 512);
   // Every ordinary load (and the q copy) is complete here: the compiler then
   // has no pending load to wait for inside the tile loop (such a wait would
   // be vmcnt(0) and drain the copies in flight).
@@ -534,11 +550,12 @@ __global__ __launch_bounds__(512) void attn_tile_kernel(AttnArgs a, int n_hg, in
     l_tot[hb] = (lbuf[0][hb][n] + lbuf[1][hb][n]) + (lbuf[2][hb][n] + lbuf[3][hb][n]);
     m_fin[hb] = mfin[hb][n];
   }
+  derotate<NHB>(o, w4, lane, a.rope_dim, rope_cs);
   if (nsplit == 1) {
-    store_output<NHB>(a, qi, h0, w4, lane, o, l_tot, m_fin, rope_cs);
+    store_output<NHB>(a, qi, h0, w4, lane, o, l_tot, m_fin);
     return;
   }
-  // partial of this split for attn_merge_kernel
+  // partial of this split for attn_merge_kernel (de-rotated)
   float* po = part + (size_t)item * AT_PART;
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt)
@@ -553,9 +570,9 @@ __global__ __launch_bounds__(512) void attn_tile_kernel(AttnArgs a, int n_hg, in
   }
 }
 
-// Merge of the NS partials of one (query, head group): rescale each to the
-// common maximum, add in split order (deterministic), divide by the sum,
-// de-rotate and store.  Block = 64 lanes covering one wave's share of the
+// Merge of the NS partials of one (query, head group) (already de-rotated):
+// rescale each to the common maximum, add in split order (deterministic),
+// divide by the sum and store.  Block = 64 lanes covering one wave's share of the
 // partial layout for two of its eight 16-dim tiles (grid: items x 16), so many
 // small blocks keep the partial reads in flight; every load is issued before
 // any arithmetic.
@@ -564,11 +581,8 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(AttnArgs a, int n_hg, in
                                                         const float* __restrict__ part) {
   const int qh = blockIdx.x >> 4, wave = (blockIdx.x >> 2) & 3, dt0 = 2 * (blockIdx.x & 3);
   const int qi = qh / n_hg, hgi = qh % n_hg;
-  const int b = qi / a.S, s = qi % a.S;
-  const int t = a.q_pos[b] + s;
   const int lane = threadIdx.x, g = lane >> 4, n = lane & 15;
   const float* pq = part + (size_t)qh * nsplit * AT_PART;
-  const int tail0 = AT_D - a.rope_dim;
   // all partial loads first (one memory round trip for up to AT_MQ splits)
   constexpr int AT_MQ = 4;
   f32x4_t v[AT_MQ][NHB][2];
@@ -622,16 +636,6 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(AttnArgs a, int n_hg, in
       float v[4];
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) v[ii] = o[j][ii] * inv_l;
-#pragma unroll
-      for (int pp = 0; pp < 2; ++pp) {
-        if (dim + 2 * pp >= tail0) {
-          float cs, sn;
-          rope_cos_sin((double)t, (dim + 2 * pp - tail0) / 2, a.rope_dim, a.log2_base, &cs, &sn);
-          const float x0 = v[2 * pp], x1 = v[2 * pp + 1];
-          v[2 * pp] = x0 * cs + x1 * sn;
-          v[2 * pp + 1] = -x0 * sn + x1 * cs;
-        }
-      }
       uint2 pk;
       pk.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
       pk.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);

@@ -6,6 +6,8 @@
 
 #include "common.hpp"
 
+#include <cmath>
+
 namespace {
 
 thread_local char g_err[512] = "";
@@ -228,6 +230,61 @@ int csa_index_topk(const void* q_idx, const float* w, const void* idx_cache, con
   if (e != hipSuccess) return launched(fn, e);
   return launched(fn, csa_host::launch_topk(scores, q_pos, topk_idx, topk_score, tws, B, S, N_cap, k, ratio,
                                             (hipStream_t)stream));
+}
+
+int csa_compress_index_topk(const void* kv_state, const void* score_state, const float* gamma, void* cache, int d,
+                            int rope_dim, int overlap, const void* idx_kv_state, const void* idx_score_state,
+                            const float* idx_gamma, void* idx_cache, int idx_rope_dim, const int32_t* state_pos0,
+                            int L, const void* q_idx, const float* w, const int32_t* q_pos, int32_t* topk_idx,
+                            float* topk_score, void* workspace, size_t workspace_bytes, int B, int S, int Hi, int di,
+                            int N_cap, int k, int ratio, unsigned flags, float eps, float rope_base, int dtype,
+                            csa_stream_t stream) {
+  const char* fn = "csa_compress_index_topk";
+  if (int rc = check_index(fn, q_idx, w, idx_cache, q_pos, B, S, Hi, di, N_cap, ratio, flags, dtype)) return rc;
+  REQ_PTR(kv_state);
+  REQ_PTR(score_state);
+  REQ_PTR(gamma);
+  REQ_PTR(cache);
+  REQ_PTR(idx_kv_state);
+  REQ_PTR(idx_score_state);
+  REQ_PTR(idx_gamma);
+  REQ_PTR(state_pos0);
+  REQ_PTR(topk_idx);
+  OPT_PTR(topk_score);
+  REQ(L >= 1, "%s: L must be >= 1", fn);
+  REQ(d >= 2 && d <= 512 && d % 2 == 0, "%s: d must be even and in [2, 512] (got %d)", fn, d);
+  REQ(di >= 2 && di <= 512 && di % 2 == 0, "%s: di must be even and in [2, 512] (got %d)", fn, di);
+  REQ(rope_dim >= 0 && rope_dim <= d && rope_dim % 2 == 0, "%s: rope_dim must be even and <= d", fn);
+  REQ(idx_rope_dim >= 0 && idx_rope_dim <= di && idx_rope_dim % 2 == 0, "%s: idx_rope_dim must be even and <= di",
+      fn);
+  REQ(ratio <= 4096, "%s: ratio must be in [1, 4096]", fn);
+  REQ(overlap == 0 || overlap == 1, "%s: overlap must be 0 or 1", fn);
+  REQ(eps >= 0.f, "%s: eps must be >= 0", fn);
+  REQ((L + ratio - 1) / ratio + 1 <= 65535 * 1024, "%s: L too large", fn);
+  REQ(k >= 1 && k <= 4096, "%s: k must be in [1, 4096] (got %d)", fn, k);
+  const size_t need = csa_index_topk_workspace_size(B, S, N_cap, k);
+  if (!workspace || workspace_bytes < need)
+    return fail(CSA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed (got %zu)", fn, need, workspace_bytes);
+  OPT_PTR(workspace);
+  const csa::CompressJob jobs[2] = {{kv_state, score_state, gamma, cache, d, rope_dim, overlap, N_cap},
+                                    {idx_kv_state, idx_score_state, idx_gamma, idx_cache, di, idx_rope_dim, 1, N_cap}};
+  float* scores = (float*)workspace;
+  void* tws = (char*)workspace + (((size_t)B * S * N_cap * sizeof(float) + 255) & ~(size_t)255);
+  const hipStream_t st = (hipStream_t)stream;
+  const int gx = (L + ratio - 1) / ratio + 1;
+  const csa::FusedCompress F{jobs[0], jobs[1], state_pos0, L, gx, B, 2 * gx * B, eps, std::log2((double)rope_base)};
+  if (csa_host::fused_compress_ok(F, S, Hi, di, N_cap, ratio, dtype)) {
+    // decode: compressors folded into the indexer (new index entries) and the top-k launch (cache rows)
+    hipError_t e = csa_host::launch_index_scores_fused(F, q_idx, w, q_pos, scores, B, S, Hi, N_cap, ratio, flags, st);
+    if (e != hipSuccess) return launched(fn, e);
+    return launched(fn, csa_host::launch_topk(scores, q_pos, topk_idx, topk_score, tws, B, S, N_cap, k, ratio, st,
+                                              &F));
+  }
+  hipError_t e = csa_host::launch_compress(jobs, 2, state_pos0, B, L, ratio, eps, rope_base, dtype, st);
+  if (e != hipSuccess) return launched(fn, e);
+  e = csa_host::launch_index_scores(q_idx, w, idx_cache, q_pos, scores, B, S, Hi, di, N_cap, ratio, flags, dtype, st);
+  if (e != hipSuccess) return launched(fn, e);
+  return launched(fn, csa_host::launch_topk(scores, q_pos, topk_idx, topk_score, tws, B, S, N_cap, k, ratio, st));
 }
 
 size_t csa_attn_workspace_size(int B, int S, int H, int D, int n_cand) {

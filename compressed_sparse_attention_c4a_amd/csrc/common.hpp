@@ -187,6 +187,17 @@ struct CompressJob {
   void* cache;
   int d, rope_dim, overlap, N_cap;
 };
+
+// Both compressors of a CSA decode step folded into the indexer and top-k
+// launches (see index.hip and topk.hip): j0 main KV, j1 index keys (j1.cache
+// is the index cache); gx group candidates per sequence, ntasks = 2*gx*B.
+struct FusedCompress {
+  CompressJob j0, j1;
+  const int32_t* pos0;
+  int L, gx, B, ntasks;
+  float eps;
+  double log2_base;
+};
 }  // namespace csa
 
 // Host-side launch helpers implemented per kernel file; called from abi.cpp.
@@ -196,9 +207,13 @@ hipError_t launch_compress(const csa::CompressJob* jobs, int njobs, const int32_
 hipError_t launch_index_scores(const void* q, const float* w, const void* K, const int32_t* q_pos, float* scores,
                                int B, int S, int Hi, int di, int N_cap, int ratio, unsigned flags, int dtype,
                                hipStream_t st);
+bool fused_compress_ok(const csa::FusedCompress& F, int S, int Hi, int di, int N_cap, int ratio, int dtype);
+hipError_t launch_index_scores_fused(const csa::FusedCompress& F, const void* q, const float* w,
+                                     const int32_t* q_pos, float* scores, int B, int S, int Hi, int N_cap, int ratio,
+                                     unsigned flags, hipStream_t st);
 size_t topk_workspace_size(int B, int S, int N_cap, int k);
 hipError_t launch_topk(const float* scores, const int32_t* q_pos, int32_t* idx, float* val, void* ws, int B, int S,
-                       int N_cap, int k, int ratio, hipStream_t st);
+                       int N_cap, int k, int ratio, hipStream_t st, const csa::FusedCompress* F = nullptr);
 size_t attn_workspace_size(int B, int S, int H, int D, int n_cand);
 hipError_t launch_attn(const void* q, const void* cmp, const int32_t* topk_idx, int k, int dense, int ratio,
                        const void* win,

@@ -1,0 +1,175 @@
+// compress_dev.hpp -- device routines of the token-level compressors C4A
+// (ratio 4, overlapping 2*ratio state) and C128A (ratio 128, non-overlapping),
+// shared by the compressor kernel and the fused compress + indexer kernel.
+//
+// "DeepSeek-V4-Pro 架构：一个 token 的旅程", sections "压缩是逐通道的 learned pooling"
+// (softmax over the token axis per channel, then RMSNorm, then RoPE on the
+// tail dims), "一个通道，逐项算出压缩结果" (entry 0 has no previous group: those
+// slots weigh 0) and "压缩条目必须等整组完成后才可见" (an entry exists once its
+// group is complete).  "图解DeepSeek V4" 2.1: a C4A entry pools the previous
+// group's first-half channels together with its own group's second-half
+// channels; 3.1: C128A pools its own 128 tokens only.
+//
+// The lane (thread) owning channel pair p = (2p, 2p+1), also a RoPE pair, runs
+// the same instruction sequence in every caller, so an entry's values do not
+// depend on which kernel computes them.
+#pragma once
+#include "common.hpp"
+
+namespace csa {
+
+// Group g = floor(p0 / ratio) + x of a sequence whose state buffer starts at
+// absolute position p0 and holds L tokens, if the compressor writes it: its
+// tokens lie in the buffer and (overlap) so do the previous group's, unless
+// g == 0.  Else -1.
+__device__ __forceinline__ long compress_group(const CompressJob& J, long p0, int x, int L, int ratio) {
+  const long g = floor_div(p0, ratio) + x;
+  const long first = g * ratio, last = first + ratio - 1;
+  if (g < 0 || g >= J.N_cap || first < p0 || last > p0 + L - 1) return -1;
+  if (J.overlap && g > 0 && first - ratio < p0) return -1;
+  return g;
+}
+
+// Scores and values of up to 16 slots (j0 .. j0+15) of channels 2p, 2p+1 of
+// entry g of sequence b; missing slots get score -inf.
+struct PoolRegs {
+  float sv[16][2], vv[16][2];
+};
+
+template <typename T>
+__device__ __forceinline__ void compress_load16(const CompressJob& J, int b, long g, long p0, int L, int ratio, int p,
+                                                int j0, PoolRegs& R) {
+  const T* __restrict__ kv = (const T*)J.kv;
+  const T* __restrict__ sc = (const T*)J.sc;
+  const int d = J.d, overlap = J.overlap;
+  const size_t row_w = (size_t)(overlap ? 2 : 1) * d;
+  const T* kvb = kv + (size_t)b * L * row_w;
+  const T* scb = sc + (size_t)b * L * row_w;
+  const long first = g * ratio;
+  const int nslot = overlap ? 2 * ratio : ratio;
+  // Every load is unconditional (a masked slot reads row 0 of the buffer and
+  // is then given score -inf), and the offsets are formed with selects: with
+  // no branch among them the 32 loads are all in flight before the first wait.
+  size_t off[16];
+  bool ok[16];
+#pragma unroll
+  for (int jj = 0; jj < 16; ++jj) {
+    const int j = j0 + jj;
+    const bool prev = overlap && j < ratio;  // slot of the previous group's half
+    ok[jj] = j < nslot && (!prev || g != 0);  // missing previous group: weight 0
+    const long tok = prev ? first - ratio + j : first + (overlap ? j - ratio : j);
+    const int ch = (overlap && !prev) ? d + 2 * p : 2 * p;
+    off[jj] = ok[jj] ? (size_t)(tok - p0) * row_w + ch : (size_t)ch;
+  }
+  float s0[16], s1[16], v0[16], v1[16];
+#pragma unroll
+  for (int jj = 0; jj < 16; ++jj) {
+    Elt<T>::ld2(scb, off[jj], s0[jj], s1[jj]);
+    Elt<T>::ld2(kvb, off[jj], v0[jj], v1[jj]);
+  }
+#pragma unroll
+  for (int jj = 0; jj < 16; ++jj) {
+    R.sv[jj][0] = ok[jj] ? s0[jj] : -INFINITY;
+    R.sv[jj][1] = ok[jj] ? s1[jj] : -INFINITY;
+    R.vv[jj][0] = ok[jj] ? v0[jj] : 0.f;
+    R.vv[jj][1] = ok[jj] ? v1[jj] : 0.f;
+  }
+}
+
+// Online-softmax fold of 16 loaded slots into (max, denominator, numerator).
+__device__ __forceinline__ void compress_fold16(const PoolRegs& R, float (&mx)[2], float (&den)[2], float (&num)[2]) {
+#pragma unroll
+  for (int jj = 0; jj < 16; ++jj)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const float sj = R.sv[jj][h];
+      if (sj == -INFINITY) continue;
+      if (sj > mx[h]) {
+        const float r = expf(mx[h] - sj);
+        den[h] *= r;
+        num[h] *= r;
+        mx[h] = sj;
+      }
+      const float e = expf(sj - mx[h]);
+      den[h] += e;
+      num[h] += e * R.vv[jj][h];
+    }
+}
+
+// Softmax-pooled value (fp32) of channels 2p, 2p+1 of entry g of sequence b
+// (2p < d).  Slots are processed in chunks of 16 whose loads are all issued
+// before any of them is used, so the memory latency is paid once per chunk.
+template <typename T>
+__device__ __forceinline__ float2 compress_pool(const CompressJob& J, int b, long g, long p0, int L, int ratio, int p) {
+  const int nslot = J.overlap ? 2 * ratio : ratio;
+  float mx[2] = {-INFINITY, -INFINITY}, den[2] = {0.f, 0.f}, num[2] = {0.f, 0.f};
+  for (int j0 = 0; j0 < nslot; j0 += 16) {
+    PoolRegs R;
+    compress_load16<T>(J, b, g, p0, L, ratio, p, j0, R);
+    compress_fold16(R, mx, den, num);
+  }
+  return make_float2(num[0] / den[0], num[1] / den[1]);
+}
+
+// Pooled value from one loaded chunk (entries with at most 16 slots).
+__device__ __forceinline__ float2 compress_pool16(const PoolRegs& R) {
+  float mx[2] = {-INFINITY, -INFINITY}, den[2] = {0.f, 0.f}, num[2] = {0.f, 0.f};
+  compress_fold16(R, mx, den, num);
+  return make_float2(num[0] / den[0], num[1] / den[1]);
+}
+
+// RMSNorm (sum of squares `tot` over the d channels), gamma, and RoPE at the
+// group's first position for the tail pairs: the stored values of pair p.
+__device__ __forceinline__ float2 compress_finish(const CompressJob& J, float2 y, float tot, long g, int ratio,
+                                                  float eps, double log2_base, int p, float gm0, float gm1) {
+  const int d = J.d;
+  const float inv = 1.0f / sqrtf(tot / (float)d + eps);
+  float a = y.x * inv * gm0, bb = y.y * inv * gm1;
+  const int tail0 = d - J.rope_dim;
+  if (2 * p >= tail0) {
+    float cs, sn;
+    rope_cos_sin((double)(g * ratio), p - tail0 / 2, J.rope_dim, log2_base, &cs, &sn);
+    const float ra = a * cs - bb * sn, rb = a * sn + bb * cs;
+    a = ra;
+    bb = rb;
+  }
+  return make_float2(a, bb);
+}
+
+// One group of 256 consecutive threads (thread p = threadIdx.x % 256 owns
+// channel pair p, d <= 512) writes entry floor(p0/ratio) + x of sequence b if
+// the compressor writes it; valid == false makes the group a bystander.
+// Every thread of the workgroup calls this (it contains a barrier).  The
+// RMSNorm sum is reduced per wave and then over the group's 4 waves in a
+// fixed order (red4: 4 floats of LDS per group); for d <= 128 only the
+// group's first wave contributes and the total equals its wave_sum exactly.
+template <typename T>
+__device__ __forceinline__ void compress_task(const CompressJob& J, const int32_t* __restrict__ pos0, int b, int x,
+                                              bool valid, int L, int ratio, float eps, double log2_base,
+                                              float* red4) {
+  const int p = threadIdx.x & 255;
+  long g = -1, p0 = 0;
+  if (valid) {
+    p0 = pos0[b];
+    g = compress_group(J, p0, x, L, ratio);
+  }
+  const bool active = g >= 0 && 2 * p < J.d;
+  float gm0 = 0.f, gm1 = 0.f;
+  float2 y = make_float2(0.f, 0.f);
+  if (active) {
+    gm0 = J.gamma[2 * p];
+    gm1 = J.gamma[2 * p + 1];
+    y = compress_pool<T>(J, b, g, p0, L, ratio, p);
+  }
+  const float ss = wave_sum(y.x * y.x + y.y * y.y);
+  if ((threadIdx.x & 63) == 0) red4[p >> 6] = ss;
+  __syncthreads();
+  const float tot = red4[0] + red4[1] + red4[2] + red4[3];
+  if (!active) return;
+  const float2 v = compress_finish(J, y, tot, g, ratio, eps, log2_base, p, gm0, gm1);
+  T* dst = (T*)J.cache + ((size_t)b * J.N_cap + g) * J.d;
+  Elt<T>::st(dst, 2 * p, v.x);
+  Elt<T>::st(dst, 2 * p + 1, v.y);
+}
+
+}  // namespace csa

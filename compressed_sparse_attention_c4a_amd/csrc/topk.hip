@@ -21,7 +21,7 @@
 // entry its slot (deterministic).  When more keys equal K* than slots remain
 // (ties across the k-th score), the ties are taken in entry order by a second,
 // contiguous pass.
-#include "common.hpp"
+#include "compress_dev.hpp"
 
 namespace csa {
 
@@ -99,12 +99,33 @@ __device__ __forceinline__ void find_digit(const uint32_t* h, int lane, uint32_t
 
 // KPT > 0: each thread holds the keys of entries tid + 1024*j, j < KPT, in
 // registers (requires N_cap <= 1024 * KPT); KPT == 0: keys are re-read.
-template <int KPT>
+// CMP: workgroups n_topk.. of the launch run the decode step's compressor
+// tasks instead (FusedCompress, four 256-thread tasks per workgroup) on the
+// CUs the top-k leaves idle; the indexer before this launch has already
+// scored the new index-key entries from its own copies of them.
+template <int KPT, bool CMP>
 __global__ __launch_bounds__(TOPK_THREADS) void topk_radix_kernel(const float* __restrict__ scores,
                                                                   const int32_t* __restrict__ q_pos,
                                                                   int32_t* __restrict__ out_idx,
                                                                   float* __restrict__ out_val, int S, int N_cap,
-                                                                  int k, int ratio) {
+                                                                  int k, int ratio, int n_topk, FusedCompress F) {
+  if constexpr (CMP) {
+    if ((int)blockIdx.x >= n_topk) {  // uniform per workgroup
+      __shared__ float red[4][4];
+      const int gq = threadIdx.x >> 8;
+      const int task = ((int)blockIdx.x - n_topk) * 4 + gq;
+      const bool valid = task < F.ntasks;
+      int z = 0, bb = 0, x = 0;
+      if (valid) {
+        z = task / (F.gx * F.B);
+        const int rem = task % (F.gx * F.B);
+        bb = rem / F.gx;
+        x = rem % F.gx;
+      }
+      compress_task<bf16>(z == 0 ? F.j0 : F.j1, F.pos0, bb, x, valid, F.L, ratio, F.eps, F.log2_base, red[gq]);
+      return;
+    }
+  }
   __shared__ __attribute__((aligned(16))) uint32_t hist[2][TOPK_BINS];
   __shared__ int2 s_w[TOPK_WAVES];
   __shared__ uint32_t s_prefix;
@@ -261,18 +282,28 @@ using namespace csa;
 
 size_t topk_workspace_size(int, int, int, int) { return 0; }
 
+template <int KPT>
+static void launch_topk_kpt(const float* scores, const int32_t* q_pos, int32_t* idx, float* val, int B, int S,
+                            int N_cap, int k, int ratio, hipStream_t st, const FusedCompress* F) {
+  const int n_topk = B * S;
+  if (F) {
+    const unsigned blocks = (unsigned)(n_topk + (F->ntasks + 3) / 4);
+    hipLaunchKernelGGL((topk_radix_kernel<KPT, true>), dim3(blocks), dim3(TOPK_THREADS), 0, st, scores, q_pos, idx,
+                       val, S, N_cap, k, ratio, n_topk, *F);
+  } else {
+    hipLaunchKernelGGL((topk_radix_kernel<KPT, false>), dim3(n_topk), dim3(TOPK_THREADS), 0, st, scores, q_pos, idx,
+                       val, S, N_cap, k, ratio, n_topk, FusedCompress{});
+  }
+}
+
 hipError_t launch_topk(const float* scores, const int32_t* q_pos, int32_t* idx, float* val, void*, int B, int S,
-                       int N_cap, int k, int ratio, hipStream_t st) {
-  const unsigned blocks = (unsigned)(B * S);
+                       int N_cap, int k, int ratio, hipStream_t st, const FusedCompress* F) {
   if (N_cap <= 8 * TOPK_THREADS)
-    hipLaunchKernelGGL(topk_radix_kernel<8>, dim3(blocks), dim3(TOPK_THREADS), 0, st, scores, q_pos, idx, val, S,
-                       N_cap, k, ratio);
+    launch_topk_kpt<8>(scores, q_pos, idx, val, B, S, N_cap, k, ratio, st, F);
   else if (N_cap <= 32 * TOPK_THREADS)
-    hipLaunchKernelGGL(topk_radix_kernel<32>, dim3(blocks), dim3(TOPK_THREADS), 0, st, scores, q_pos, idx, val, S,
-                       N_cap, k, ratio);
+    launch_topk_kpt<32>(scores, q_pos, idx, val, B, S, N_cap, k, ratio, st, F);
   else
-    hipLaunchKernelGGL(topk_radix_kernel<0>, dim3(blocks), dim3(TOPK_THREADS), 0, st, scores, q_pos, idx, val, S,
-                       N_cap, k, ratio);
+    launch_topk_kpt<0>(scores, q_pos, idx, val, B, S, N_cap, k, ratio, st, F);
   return hipGetLastError();
 }
 

@@ -1,6 +1,6 @@
 """One pass of the compressed attention hot path on device tensors:
 
-    csa_compress_kv_index (main KV and index keys) -> csa_index_topk
+    csa_compress_index_topk (both compressors, index scores, top-k)
       -> csa_sparse_attn                                  (CSA layers)
     csa_compress (C128A) -> hca_attn                      (HCA layers)
 
@@ -63,13 +63,12 @@ class Step:
             return lambda: fn(*a, **kw, stream=stream)
 
         if sh.indexer:
-            # both compressors (main KV and index keys) in one launch
-            c = [("compress", thunk(K.csa_compress_kv_index, dev["kv_state"], dev["score_state"], dev["gamma"],
-                                    dev["cmp_cache"], dev["idx_kv_state"], dev["idx_score_state"], dev["idx_gamma"],
-                                    dev["idx_cache"], dev["state_pos0"], ratio=sh.ratio, overlap=sh.overlap,
-                                    rope_dim=sh.rope, idx_rope_dim=sh.idx_rope))]
-            c.append(("index_topk", thunk(K.csa_index_topk, dev["q_idx"], dev["w"], dev["idx_cache"], dev["q_pos"],
-                                          self.topk_idx, ratio=sh.ratio, workspace=self.idx_ws)))
+            # both compressors (main KV and index keys), index scores and top-k
+            c = [("compress_index_topk",
+                  thunk(K.csa_compress_index_topk, dev["kv_state"], dev["score_state"], dev["gamma"], dev["cmp_cache"],
+                        dev["idx_kv_state"], dev["idx_score_state"], dev["idx_gamma"], dev["idx_cache"],
+                        dev["state_pos0"], dev["q_idx"], dev["w"], dev["q_pos"], self.topk_idx, ratio=sh.ratio,
+                        overlap=sh.overlap, rope_dim=sh.rope, idx_rope_dim=sh.idx_rope, workspace=self.idx_ws))]
             c.append(("attn", thunk(K.csa_sparse_attn, dev["q"], dev["cmp_cache"], self.topk_idx, dev["win_kv"],
                                     dev.get("win_pos0"), dev["sink"], dev["q_pos"], self.out, self.lse,
                                     rope_dim=sh.rope, window=sh.window, workspace=self.attn_ws)))

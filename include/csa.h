@@ -145,6 +145,27 @@ int csa_index_topk(const void* q_idx, const float* w, const void* idx_cache, con
                    int Hi, int di, int N_cap, int k, int ratio, unsigned flags, int dtype, csa_stream_t stream);
 
 /*
+ * csa_compress_index_topk -- csa_compress_kv_index followed by csa_index_topk
+ * over the index cache it writes ([P1] "少读 KV 之前，Indexer 仍要给历史打分": the
+ * indexer scores the entries the compressor has completed, this step's
+ * included; [P5] 2.2).  Arguments as in those two calls; both caches hold
+ * N_cap entries (cache [B, N_cap, d], idx_cache [B, N_cap, di]) and the
+ * index-key compressor always overlaps.  Results are identical to the two
+ * calls.  When every query is a single position per sequence (S == 1), the
+ * state buffer holds at most 2*ratio tokens (decode) and the indexer takes
+ * its MFMA path, the compressors run inside the indexer launch: the wave that
+ * scores a freshly written index entry computes that entry itself, so no
+ * workgroup waits for another.  workspace: csa_index_topk_workspace_size.
+ */
+int csa_compress_index_topk(const void* kv_state, const void* score_state, const float* gamma, void* cache, int d,
+                            int rope_dim, int overlap, const void* idx_kv_state, const void* idx_score_state,
+                            const float* idx_gamma, void* idx_cache, int idx_rope_dim, const int32_t* state_pos0,
+                            int L, const void* q_idx, const float* w, const int32_t* q_pos, int32_t* topk_idx,
+                            float* topk_score, void* workspace, size_t workspace_bytes, int B, int S, int Hi, int di,
+                            int N_cap, int k, int ratio, unsigned flags, float eps, float rope_base, int dtype,
+                            csa_stream_t stream);
+
+/*
  * csa_sparse_attn -- multi-query attention over the window plus the selected
  * compressed entries, [P1] "局部和压缩记忆，共用一次归一化" (one candidate set, one
  * softmax, per-head sink adds to the denominator only), "输出投影也分组…"

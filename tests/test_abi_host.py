@@ -63,6 +63,27 @@ def test_index_and_topk_validation(lib):
                               None) == CSA_ERR_WORKSPACE
 
 
+def _cit(lib, kv=P, idx_cache=P, pos0=P, topk=P, ws=P, ws_bytes=1 << 30, d=512, di=128, L=8, k=16, ratio=4):
+    """csa_compress_index_topk with valid-looking host arguments (no launch
+    happens: every case below fails validation first)."""
+    return lib.csa_compress_index_topk(kv, P, P, P, d, 64, 1, P, P, P, idx_cache, 64, pos0, L, P, P, P, topk, None,
+                                       ws, ws_bytes, 2, 1, 64, di, 100, k, ratio, 0, 1e-6, 10000.0, 1, None)
+
+
+def test_compress_index_topk_validation(lib):
+    assert _cit(lib, kv=None) == CSA_ERR_NULL
+    assert _cit(lib, idx_cache=None) == CSA_ERR_NULL
+    assert _cit(lib, pos0=None) == CSA_ERR_NULL
+    assert _cit(lib, topk=None) == CSA_ERR_NULL
+    assert _cit(lib, kv=MIS) == CSA_ERR_ALIGN
+    assert _cit(lib, d=513) == CSA_ERR_SHAPE
+    assert _cit(lib, L=0) == CSA_ERR_SHAPE
+    assert _cit(lib, k=0) == CSA_ERR_SHAPE
+    need = lib.csa_index_topk_workspace_size(2, 1, 100, 16)
+    assert _cit(lib, ws_bytes=need - 1) == CSA_ERR_WORKSPACE
+    assert _cit(lib, ws=None) == CSA_ERR_WORKSPACE
+
+
 def _attn(lib, q=P, cmp=P, idx=P, win=P, wp=None, sink=P, qp=P, out=P, lse=None, B=1, S=1, H=128, D=512, rope=64,
           N=100, k=16, W=128, window=128, dtype=1):
     return lib.csa_sparse_attn(q, cmp, idx, win, wp, sink, qp, out, lse, None, 0, B, S, H, D, rope, N, k, W, window,

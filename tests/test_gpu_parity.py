@@ -96,6 +96,66 @@ def test_paired_compress_equals_two_calls(case):
     np.testing.assert_array_equal(raw_np(a["idx_cache"]), raw_np(b["idx_cache"]))
 
 
+def _separate_and_fused(inp):
+    """csa_compress_kv_index + csa_index_topk on one device copy of the
+    inputs, csa_compress_index_topk on another; returns both copies with
+    their top-k lists and workspaces."""
+    sh = inp["shape"]
+    out = []
+    for fused in (False, True):
+        d = P.to_device(inp)
+        idx = torch.empty((sh.B, sh.S, sh.k), dtype=torch.int32, device="cuda")
+        ws = torch.empty(K.csa_index_topk_workspace_size(sh.B, sh.S, sh.N_cap, sh.k), dtype=torch.uint8,
+                         device="cuda")
+        if fused:
+            K.csa_compress_index_topk(d["kv_state"], d["score_state"], d["gamma"], d["cmp_cache"], d["idx_kv_state"],
+                                      d["idx_score_state"], d["idx_gamma"], d["idx_cache"], d["state_pos0"],
+                                      d["q_idx"], d["w"], d["q_pos"], idx, ratio=sh.ratio, overlap=sh.overlap,
+                                      rope_dim=sh.rope, idx_rope_dim=sh.idx_rope, workspace=ws)
+        else:
+            K.csa_compress_kv_index(d["kv_state"], d["score_state"], d["gamma"], d["cmp_cache"], d["idx_kv_state"],
+                                    d["idx_score_state"], d["idx_gamma"], d["idx_cache"], d["state_pos0"],
+                                    ratio=sh.ratio, overlap=sh.overlap, rope_dim=sh.rope, idx_rope_dim=sh.idx_rope)
+            K.csa_index_topk(d["q_idx"], d["w"], d["idx_cache"], d["q_pos"], idx, ratio=sh.ratio, workspace=ws)
+        out.append((d, idx, ws))
+    return out
+
+
+def _assert_fused_equal(inp):
+    sh = inp["shape"]
+    (a, ia, wa), (b, ib, wb) = _separate_and_fused(inp)
+    np.testing.assert_array_equal(raw_np(a["cmp_cache"]), raw_np(b["cmp_cache"]))
+    np.testing.assert_array_equal(raw_np(a["idx_cache"]), raw_np(b["idx_cache"]))
+    n = sh.B * sh.S * sh.N_cap
+    np.testing.assert_array_equal(wa[:4 * n].view(torch.float32).cpu().numpy(),
+                                  wb[:4 * n].view(torch.float32).cpu().numpy())   # the scores, bit for bit
+    np.testing.assert_array_equal(ia.cpu().numpy(), ib.cpu().numpy())
+
+
+def test_fused_compress_index_topk_equals_separate_calls(case):
+    """csa_compress_index_topk (fused launch for decode, two launches
+    otherwise) writes the same caches, scores and top-k as the separate calls."""
+    name, inp, _ = case
+    if not inp["shape"].indexer:
+        pytest.skip("HCA has no indexer")
+    _assert_fused_equal(inp)
+
+
+def test_fused_decode_new_entry_at_tile_and_chunk_edges():
+    """Decode at full N_cap with the freshly written index entry at the
+    first/last row of a wave tile, of a workgroup chunk and of the cache: the
+    wave that scores it computes it in the fused launch."""
+    entries = [0, 31, 32, 255, 256, 4095, 5000, 8191]
+    q_pos = [4 * e + 3 for e in entries]
+    sh = W.Shape(name="csa_decode_edges", B=len(entries), S=1, N_cap=8192, window=128, W_cap=128, state_len=8,
+                 k=1024, seed=21)
+    inp = dict(W.generate(sh))
+    inp["q_pos"] = np.asarray(q_pos, dtype=np.int32)
+    inp["state_pos0"] = (inp["q_pos"] - 7).astype(np.int32)
+    print(f"[fused] entries {entries}", flush=True)
+    _assert_fused_equal(inp)
+
+
 def test_index_score_stage(case, orc):
     name, inp, ref = case
     sh = inp["shape"]

@@ -161,12 +161,11 @@ __global__ __launch_bounds__(64) void attn_generic_kernel(AttnArgs a) {
 // an item's tiles are divided between NS workgroups, each of which writes its
 // unnormalised O, running max and sum to the workspace; attn_merge_kernel
 // (launched next on the same stream) combines them at the common maximum.
-// Rows are XOR-swizzled in LDS: 16-byte granule c of tile row r sits at
-// c ^ swz(r), swz(r) = 2*(r & 3) + ((r >> 2) & 1) + (r & 8).  Any 8
-// consecutive rows from a multiple of 8 get distinct swizzles modulo 8, and
-// any 4 from a multiple of 4 differ in bits 1-2: the row reads of QK^T (8
-// rows of one granule per 128-byte LDS cycle) and the transposed reads of
-// P.V (4 rows x 2 adjacent granules) hit distinct banks.
+// LDS rows are 1088 bytes apart (64 bytes of padding, no permutation): the
+// row reads of QK^T (ds_read_b128) and the transposed reads of P.V
+// (ds_read_b64_tr_b16) then run at 113-117 B/clk/CU on gfx950, against 95-101
+// for XOR-swizzled 1024-byte rows (a probe of exactly these access
+// patterns), and every address is one lane base plus immediates.
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
@@ -174,7 +173,8 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 constexpr int AT_D = 512;
 constexpr int AT_ROWB = AT_D * 2;
 constexpr int AT_TR = 64;                       // rows per tile
-constexpr int AT_TILE_B = AT_TR * AT_ROWB;
+constexpr int AT_RS = AT_ROWB + 64;            // LDS bytes per tile row (64 bytes of padding)
+constexpr int AT_TILE_B = AT_TR * AT_RS;
 constexpr int AT_MAXK = 2048;                   // sparse lists up to this many entries
 constexpr int AT_MAXWIN = 1024;                 // windows up to this many rows
 constexpr int AT_LIST = AT_MAXWIN + AT_MAXK;    // candidate slots resolved in LDS
@@ -182,8 +182,6 @@ constexpr int AT_PST = AT_TR + 8;               // bf16 per P row (padded agains
 constexpr int AT_PART = 4 * 8 * 2 * 64 * 4 + 64;  // floats of one partial: O (lane layout), then (m, l) per head
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float AT_SLACK = 16.f;                // log2 headroom of the lazily updated running max
-
-__device__ __forceinline__ int ar_swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1) | (r & 8); }
 
 // Offset (floats) of lane `lane`'s O^T fragment (dim tile dt, head block hb)
 // of dim slice `v` inside a partial.
@@ -299,7 +297,7 @@ __global__ __launch_bounds__(512) void attn_tile_kernel(AttnArgs a, int n_hg, in
 #pragma unroll
     for (int rr = 0; rr < HG / 4; ++rr) {
       const int r = w4 * (HG / 4) + rr;
-      dma16_sbase(qb + (size_t)r * AT_ROWB, 16u * (uint32_t)(lane ^ ar_swz(r)), ring[1] + r * AT_ROWB);
+      dma16_sbase(qb + (size_t)r * AT_ROWB, 16u * (uint32_t)lane, ring[1] + r * AT_RS);
     }
 #pragma unroll
     for (int hb = 0; hb < NHB; ++hb) sinkv[hb] = a.sink[h0 + 16 * hb + n];
@@ -364,7 +362,7 @@ __global__ __launch_bounds__(512) void attn_tile_kernel(AttnArgs a, int n_hg, in
     for (int rr = 0; rr < 16; ++rr) {
       const int id = ids[rr];
       const char* row = id >= 0 ? cmpb + (size_t)(uint32_t)id * AT_ROWB : winb + (size_t)(uint32_t)(-1 - id) * AT_ROWB;
-      dma16_sbase(row, 16u * (uint32_t)(lane ^ ar_swz(rr)), ring[ti & 1] + (16 * w4 + rr) * AT_ROWB);
+      dma16_sbase(row, 16u * (uint32_t)lane, ring[ti & 1] + (16 * w4 + rr) * AT_RS);
     }
   };
   auto tile_mask = [&](int ti) -> uint64_t {
@@ -386,10 +384,9 @@ __global__ __launch_bounds__(512) void attn_tile_kernel(AttnArgs a, int n_hg, in
     bf16x8_t qf[NHB][16];
 #pragma unroll
     for (int hb = 0; hb < NHB; ++hb) {
-      const uint8_t* qr = ring[1] + (16 * hb + n) * AT_ROWB;
-      const int sw = ar_swz(16 * hb + n);
+      const uint8_t* qr = ring[1] + (16 * hb + n) * AT_RS + 16 * g;
 #pragma unroll
-      for (int kk = 0; kk < 16; ++kk) qf[hb][kk] = *(const bf16x8_t*)(qr + 16 * ((4 * kk + g) ^ sw));
+      for (int kk = 0; kk < 16; ++kk) qf[hb][kk] = *(const bf16x8_t*)(qr + 64 * kk);
     }
     const float sc2 = a.scale * LOG2E;
 #pragma unroll
@@ -397,10 +394,9 @@ __global__ __launch_bounds__(512) void attn_tile_kernel(AttnArgs a, int n_hg, in
       m_run[hb] = sinkv[hb] * LOG2E;
       l_run[hb] = (split == 0 && w4 == 0 && g == 0 && sinkv[hb] != -INFINITY) ? 1.f : 0.f;
     }
-    const int rsw = ar_swz(n);  // swizzle of this lane's row (16*w4 + n)
     lds_barrier();              // X_0 (every wave has its q fragments before tile 1 is copied)
     for (int i = 0; i < ntiles; ++i) {
-      const uint8_t* myrow = ring[i & 1] + (16 * w4 + n) * AT_ROWB;
+      const uint8_t* myrow = ring[i & 1] + (16 * w4 + n) * AT_RS + 16 * g;
       // 1. logits of this wave's 16 rows for the HG heads (two chains per head block)
       f32x4_t S0[NHB], S1[NHB];
 #pragma unroll
@@ -411,7 +407,7 @@ __global__ __launch_bounds__(512) void attn_tile_kernel(AttnArgs a, int n_hg, in
 #pragma unroll
         for (int k2 = 0; k2 < 8; ++k2) {
           const int kk = 8 * half + k2;
-          rf[k2] = *(const bf16x8_t*)(myrow + 16 * ((4 * kk + g) ^ rsw));
+          rf[k2] = *(const bf16x8_t*)(myrow + 64 * kk);
         }
 #pragma unroll
         for (int k2 = 0; k2 < 8; k2 += 2) {
@@ -491,7 +487,8 @@ __global__ __launch_bounds__(512) void attn_tile_kernel(AttnArgs a, int n_hg, in
   } else {
     // ---------------------------------------------------------------- O waves
     const int d0 = w4 * 128;            // P.V dim slice of this wave
-    const int trow = 8 * g + (n >> 2);  // transposed-read row for k-chunk 0 (add 32c, +4)
+    // transposed reads: rows 32c + 8g + (n >> 2) (+4), dims d0 + 16dt + 4(n & 3)
+    const int tr_off = (8 * g + (n >> 2)) * AT_RS + 2 * d0 + 8 * (n & 3);
     if (ntiles > 0) copy_tile(0);
     WAIT_VMCNT(0);
     lds_barrier();  // X_0
@@ -514,19 +511,13 @@ __global__ __launch_bounds__(512) void attn_tile_kernel(AttnArgs a, int n_hg, in
         bf16x8_t pf[NHB];
 #pragma unroll
         for (int hb = 0; hb < NHB; ++hb) pf[hb] = *(const bf16x8_t*)&pbuf[16 * hb + n][32 * c + 8 * g];
-        const int ra = 32 * c + trow, rb = ra + 4;
-        const uint8_t* pa = tile + ra * AT_ROWB;
-        const uint8_t* pb = tile + rb * AT_ROWB;
-        const int sa = ar_swz(ra), sb = ar_swz(rb);
+        const uint8_t* pa = tile + tr_off + 32 * c * AT_RS;
+        const uint8_t* pb = pa + 4 * AT_RS;
         bf16x4_t lo[8], hi[8];
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) {
-          const int dim = d0 + 16 * dt + 4 * (n & 3);
-          const int gr = dim >> 3, hf = (dim >> 2) & 1;
-          lo[dt] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-              (__attribute__((address_space(3))) bf16x4_t*)(pa + 16 * (gr ^ sa) + 8 * hf));
-          hi[dt] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-              (__attribute__((address_space(3))) bf16x4_t*)(pb + 16 * (gr ^ sb) + 8 * hf));
+          lo[dt] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4_t*)(pa + 32 * dt));
+          hi[dt] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4_t*)(pb + 32 * dt));
         }
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) {

@@ -179,12 +179,15 @@ constexpr int AT_MAXK = 2048;                   // sparse lists up to this many 
 constexpr int AT_MAXWIN = 1024;                 // windows up to this many rows
 constexpr int AT_LIST = AT_MAXWIN + AT_MAXK;    // candidate slots resolved in LDS
 constexpr int AT_PST = AT_TR + 8;               // bf16 per P row (padded against bank conflicts)
-constexpr int AT_PART = 4 * 8 * 2 * 64 * 4 + 64;  // floats of one partial: O (lane layout), then (m, l) per head
+// One split's partial: O / l as bf16 in the lane layout (4 slices x 8 dim
+// tiles x 2 head blocks x 64 lanes x 4), then (m, l) per head as fp32.
+constexpr int AT_PART_O = 4 * 8 * 2 * 64 * 4;    // bf16 elements of the O part
+constexpr int AT_PART_B = AT_PART_O * 2 + 64 * 4;  // bytes of one partial
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float AT_SLACK = 16.f;                // log2 headroom of the lazily updated running max
 
-// Offset (floats) of lane `lane`'s O^T fragment (dim tile dt, head block hb)
-// of dim slice `v` inside a partial.
+// Offset (elements) of lane `lane`'s O^T fragment (dim tile dt, head block hb)
+// of dim slice `v` inside a partial's O part.
 __device__ __forceinline__ int part_off(int v, int dt, int hb, int lane) {
   return (((v * 8 + dt) * 2 + hb) * 64 + lane) * 4;
 }
@@ -546,17 +549,28 @@ __global__ __launch_bounds__(512) void attn_tile_kernel(AttnArgs a, int n_hg, in
     store_output<NHB>(a, qi, h0, w4, lane, o, l_tot, m_fin);
     return;
   }
-  // partial of this split for attn_merge_kernel (de-rotated)
-  float* po = part + (size_t)item * AT_PART;
+  // partial of this split for attn_merge_kernel: the de-rotated O divided by
+  // this split's sum (a convex combination of rows, so bf16 keeps the range),
+  // and (m, l) in fp32
+  uint8_t* pb = (uint8_t*)part + (size_t)item * AT_PART_B;
+  bf16* po = (bf16*)pb;
+  float* pml = (float*)(pb + AT_PART_O * 2);
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt)
+  for (int hb = 0; hb < NHB; ++hb) {
+    const float inv_l = l_tot[hb] > 0.f ? 1.f / l_tot[hb] : 0.f;
 #pragma unroll
-    for (int hb = 0; hb < NHB; ++hb) *(f32x4_t*)(po + part_off(w4, dt, hb, lane)) = o[dt][hb];
+    for (int dt = 0; dt < 8; ++dt) {
+      uint2 pk;
+      pk.x = (uint32_t)f2bf(o[dt][hb][0] * inv_l) | ((uint32_t)f2bf(o[dt][hb][1] * inv_l) << 16);
+      pk.y = (uint32_t)f2bf(o[dt][hb][2] * inv_l) | ((uint32_t)f2bf(o[dt][hb][3] * inv_l) << 16);
+      *(uint2*)(po + part_off(w4, dt, hb, lane)) = pk;
+    }
+  }
   if (w4 == 0 && g == 0) {
 #pragma unroll
     for (int hb = 0; hb < NHB; ++hb) {
-      po[AT_PART - 64 + (16 * hb + n) * 2] = m_fin[hb];
-      po[AT_PART - 64 + (16 * hb + n) * 2 + 1] = l_tot[hb];
+      pml[(16 * hb + n) * 2] = m_fin[hb];
+      pml[(16 * hb + n) * 2 + 1] = l_tot[hb];
     }
   }
 }
@@ -569,54 +583,59 @@ __global__ __launch_bounds__(512) void attn_tile_kernel(AttnArgs a, int n_hg, in
 // any arithmetic.
 template <int NHB>
 __global__ __launch_bounds__(64) void attn_merge_kernel(AttnArgs a, int n_hg, int nsplit,
-                                                        const float* __restrict__ part) {
+                                                        const uint8_t* __restrict__ part) {
   const int qh = blockIdx.x >> 4, wave = (blockIdx.x >> 2) & 3, dt0 = 2 * (blockIdx.x & 3);
   const int qi = qh / n_hg, hgi = qh % n_hg;
   const int lane = threadIdx.x, g = lane >> 4, n = lane & 15;
-  const float* pq = part + (size_t)qh * nsplit * AT_PART;
+  const uint8_t* pq = part + (size_t)qh * nsplit * AT_PART_B;
+  auto po = [&](int s2) { return (const bf16*)(pq + (size_t)s2 * AT_PART_B); };
+  auto pml = [&](int s2) { return (const float*)(pq + (size_t)s2 * AT_PART_B + AT_PART_O * 2); };
+  auto unpack = [](uint2 u) {
+    return f32x4_t{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u), __uint_as_float(u.y << 16),
+                   __uint_as_float(u.y & 0xFFFF0000u)};
+  };
   // all partial loads first (one memory round trip for up to AT_MQ splits)
   constexpr int AT_MQ = 4;
-  f32x4_t v[AT_MQ][NHB][2];
+  uint2 v[AT_MQ][NHB][2];
   float2 ml[AT_MQ][NHB];
   const int nq = nsplit < AT_MQ ? nsplit : AT_MQ;
 #pragma unroll
   for (int s2 = 0; s2 < AT_MQ; ++s2) {
     if (s2 < nq) {
-      const float* ps = pq + (size_t)s2 * AT_PART;
 #pragma unroll
       for (int hb = 0; hb < NHB; ++hb) {
-        v[s2][hb][0] = *(const f32x4_t*)(ps + part_off(wave, dt0, hb, lane));
-        v[s2][hb][1] = *(const f32x4_t*)(ps + part_off(wave, dt0 + 1, hb, lane));
-        ml[s2][hb] = *(const float2*)(ps + AT_PART - 64 + (16 * hb + n) * 2);
+        v[s2][hb][0] = *(const uint2*)(po(s2) + part_off(wave, dt0, hb, lane));
+        v[s2][hb][1] = *(const uint2*)(po(s2) + part_off(wave, dt0 + 1, hb, lane));
+        ml[s2][hb] = *(const float2*)(pml(s2) + (16 * hb + n) * 2);
       }
     }
   }
 #pragma unroll
   for (int hb = 0; hb < NHB; ++hb) {
-    const int mi = AT_PART - 64 + (16 * hb + n) * 2;
+    const int mi = (16 * hb + n) * 2;
     float mx = -INFINITY;
 #pragma unroll
     for (int s2 = 0; s2 < AT_MQ; ++s2)
       if (s2 < nq) mx = fmaxf(mx, ml[s2][hb].x);
-    for (int s2 = AT_MQ; s2 < nsplit; ++s2) mx = fmaxf(mx, pq[(size_t)s2 * AT_PART + mi]);
+    for (int s2 = AT_MQ; s2 < nsplit; ++s2) mx = fmaxf(mx, pml(s2)[mi]);
     const float mref = (mx == -INFINITY) ? 0.f : mx;
+    // weight of split s: l_s * exp2(m_s - max); out = sum w_s (O_s / l_s) / sum w_s
     float l = 0.f;
     f32x4_t o[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int s2 = 0; s2 < AT_MQ; ++s2) {
       if (s2 < nq) {
-        const float fs = __builtin_amdgcn_exp2f(ml[s2][hb].x - mref);
-        l += ml[s2][hb].y * fs;
-        o[0] += fs * v[s2][hb][0];
-        o[1] += fs * v[s2][hb][1];
+        const float ws = ml[s2][hb].y * __builtin_amdgcn_exp2f(ml[s2][hb].x - mref);
+        l += ws;
+        o[0] += ws * unpack(v[s2][hb][0]);
+        o[1] += ws * unpack(v[s2][hb][1]);
       }
     }
     for (int s2 = AT_MQ; s2 < nsplit; ++s2) {
-      const float* ps = pq + (size_t)s2 * AT_PART;
-      const float fs = __builtin_amdgcn_exp2f(ps[mi] - mref);
-      l += ps[mi + 1] * fs;
-      o[0] += fs * *(const f32x4_t*)(ps + part_off(wave, dt0, hb, lane));
-      o[1] += fs * *(const f32x4_t*)(ps + part_off(wave, dt0 + 1, hb, lane));
+      const float ws = pml(s2)[mi + 1] * __builtin_amdgcn_exp2f(pml(s2)[mi] - mref);
+      l += ws;
+      o[0] += ws * unpack(*(const uint2*)(po(s2) + part_off(wave, dt0, hb, lane)));
+      o[1] += ws * unpack(*(const uint2*)(po(s2) + part_off(wave, dt0 + 1, hb, lane)));
     }
     const float inv_l = 1.f / l;
     const int h = hgi * 16 * NHB + 16 * hb + n;
@@ -624,12 +643,12 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(AttnArgs a, int n_hg, in
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int dim = wave * 128 + 16 * (dt0 + j) + 4 * g;
-      float v[4];
+      float x[4];
 #pragma unroll
-      for (int ii = 0; ii < 4; ++ii) v[ii] = o[j][ii] * inv_l;
+      for (int ii = 0; ii < 4; ++ii) x[ii] = o[j][ii] * inv_l;
       uint2 pk;
-      pk.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
-      pk.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
+      pk.x = (uint32_t)f2bf(x[0]) | ((uint32_t)f2bf(x[1]) << 16);
+      pk.y = (uint32_t)f2bf(x[2]) | ((uint32_t)f2bf(x[3]) << 16);
       *(uint2*)(outp + dim) = pk;
     }
     if (a.lse && wave == 0 && dt0 == 0 && g == 0) a.lse[(size_t)qi * a.H + h] = (mx + log2f(l)) / LOG2E;
@@ -661,7 +680,7 @@ static AttnPlan attn_plan(long Q, int H, int n_cand) {
   ns = ns > 16 ? 16 : ns;
   p.nsplit = ns < 1 ? 1 : (int)ns;
   p.total = (int)(items * p.nsplit);
-  p.ws_bytes = p.nsplit > 1 ? (size_t)p.total * AT_PART * 4 : 0;
+  p.ws_bytes = p.nsplit > 1 ? (size_t)p.total * AT_PART_B : 0;
   return p;
 }
 
@@ -685,11 +704,11 @@ hipError_t launch_attn(const void* q, const void* cmp, const int32_t* topk_idx, 
     if (p.nhb == 2) {
       hipLaunchKernelGGL((attn_tile_kernel<2>), dim3(p.total), dim3(512), 0, st, a, p.n_hg, p.nsplit, p.total, part);
       if (p.nsplit > 1)
-        hipLaunchKernelGGL((attn_merge_kernel<2>), dim3(items * 16), dim3(64), 0, st, a, p.n_hg, p.nsplit, part);
+        hipLaunchKernelGGL((attn_merge_kernel<2>), dim3(items * 16), dim3(64), 0, st, a, p.n_hg, p.nsplit, (const uint8_t*)part);
     } else {
       hipLaunchKernelGGL((attn_tile_kernel<1>), dim3(p.total), dim3(512), 0, st, a, p.n_hg, p.nsplit, p.total, part);
       if (p.nsplit > 1)
-        hipLaunchKernelGGL((attn_merge_kernel<1>), dim3(items * 16), dim3(64), 0, st, a, p.n_hg, p.nsplit, part);
+        hipLaunchKernelGGL((attn_merge_kernel<1>), dim3(items * 16), dim3(64), 0, st, a, p.n_hg, p.nsplit, (const uint8_t*)part);
     }
     return hipGetLastError();
   }

@@ -118,3 +118,20 @@ def test_sink_minus_infinity_and_no_rope(orc, B, H, N_cap, k, q_pos):
     ref, _, _ = orc.attn(x["q"], x["cmp"], x["win"], sink, x["q_pos"], topk_idx=x["topk"], window=128, rope_dim=0,
                          scale=0.03)
     assert_close(to_np(out), ref, TOL["bf16"], "no sink, no rope")
+
+
+@pytest.mark.parametrize("H,q_pos", [(128, [5000, 90, 0]), (48, [300, 127, 1])])
+def test_window_only_layer(orc, H, q_pos):
+    """A sliding-window-only layer (window plus sink, no compressed channel):
+    csa_sparse_attn with an empty selection (k = 0)."""
+    B, S = len(q_pos), 1
+    x = _inputs(11, B, S, H, 64, 128, 1, q_pos)
+    topk = torch.empty((B, S, 0), dtype=torch.int32, device="cuda")
+    out = torch.empty((B, S, H, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, S, H), dtype=torch.float32, device="cuda")
+    K.csa_sparse_attn(_dev(x["q"]), _dev(x["cmp"]), topk, _dev(x["win"]), None, _dev(x["sink"]), _dev(x["q_pos"]),
+                      out, lse, rope_dim=64, window=128)
+    ref, rlse, _ = orc.attn(x["q"], x["cmp"], x["win"], x["sink"], x["q_pos"],
+                            topk_idx=np.zeros((B, S, 0), dtype=np.int32), window=128, rope_dim=64)
+    assert_close(to_np(out), ref, TOL["bf16"], "window only: output")
+    assert_close(lse.cpu().numpy(), rlse, 1e-3, "window only: lse")

@@ -172,4 +172,72 @@ __device__ __forceinline__ void compress_task(const CompressJob& J, const int32_
   Elt<T>::st(dst, 2 * p + 1, v.y);
 }
 
+// Wide form for entries with many slots (C128A: 128 tokens): a workgroup of
+// 1024 threads, thread (p = tid % 256, q = tid / 256) folds slots q*SQ ..
+// q*SQ+SQ-1 (SQ = nslot/4, in chunks of 16) of channel pair p; the four
+// partial softmax states of a pair are then combined in q order through LDS
+// (red: 4*256 float4 of LDS), and the first 256 threads finish the entry as
+// compress_task does.  Four times the loads in flight per round trip.
+template <typename T>
+__device__ __forceinline__ void compress_task_wide(const CompressJob& J, const int32_t* __restrict__ pos0, int b, int x,
+                                                   int L, int ratio, float eps, double log2_base, float4* red,
+                                                   float* red4) {
+  const int p = threadIdx.x & 255, q = threadIdx.x >> 8;
+  const long p0 = pos0[b];
+  const long g = compress_group(J, p0, x, L, ratio);
+  if (g < 0) return;  // uniform: depends on (b, x) only
+  const bool active = 2 * p < J.d;
+  const int nslot = J.overlap ? 2 * ratio : ratio;
+  const int sq = (nslot + 3) / 4;
+  float mx[2] = {-INFINITY, -INFINITY}, den[2] = {0.f, 0.f}, num[2] = {0.f, 0.f};
+  if (active) {
+    for (int j0 = q * sq; j0 < min(nslot, (q + 1) * sq); j0 += 16) {
+      PoolRegs R;
+      compress_load16<T>(J, b, g, p0, L, ratio, p, j0, R);
+      // slots of the next quarter belong to another thread
+#pragma unroll
+      for (int jj = 0; jj < 16; ++jj)
+        if (j0 + jj >= (q + 1) * sq) R.sv[jj][0] = R.sv[jj][1] = -INFINITY;
+      compress_fold16(R, mx, den, num);
+    }
+  }
+  red[threadIdx.x] = make_float4(mx[0], mx[1], den[0], den[1]);
+  red[1024 + threadIdx.x] = make_float4(num[0], num[1], 0.f, 0.f);
+  __syncthreads();
+  float2 y = make_float2(0.f, 0.f);
+  if (q == 0 && active) {
+    float m2[2] = {-INFINITY, -INFINITY}, d2[2] = {0.f, 0.f}, n2[2] = {0.f, 0.f};
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+      const float4 a = red[qq * 256 + p], c = red[1024 + qq * 256 + p];
+      const float qm[2] = {a.x, a.y}, qd[2] = {a.z, a.w}, qn[2] = {c.x, c.y};
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        if (qm[h] == -INFINITY) continue;  // no slot in this quarter
+        if (qm[h] > m2[h]) {
+          const float r = expf(m2[h] - qm[h]);
+          d2[h] *= r;
+          n2[h] *= r;
+          m2[h] = qm[h];
+        }
+        const float r = expf(qm[h] - m2[h]);
+        d2[h] += qd[h] * r;
+        n2[h] += qn[h] * r;
+      }
+    }
+    y = make_float2(n2[0] / d2[0], n2[1] / d2[1]);
+  }
+  if (q == 0) {
+    const float ss = wave_sum(y.x * y.x + y.y * y.y);
+    if ((threadIdx.x & 63) == 0) red4[threadIdx.x >> 6] = ss;
+  }
+  __syncthreads();
+  if (q != 0 || !active) return;
+  const float tot = red4[0] + red4[1] + red4[2] + red4[3];
+  const float2 v = compress_finish(J, y, tot, g, ratio, eps, log2_base, p, J.gamma[2 * p], J.gamma[2 * p + 1]);
+  T* dst = (T*)J.cache + ((size_t)b * J.N_cap + g) * J.d;
+  Elt<T>::st(dst, 2 * p, v.x);
+  Elt<T>::st(dst, 2 * p + 1, v.y);
+}
+
 }  // namespace csa

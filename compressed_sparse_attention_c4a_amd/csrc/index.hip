@@ -102,7 +102,6 @@ __global__ __launch_bounds__(256) void index_scores_mfma(const bf16* __restrict_
   constexpr int HI = 16 * MT;
   __shared__ __attribute__((aligned(16))) uint8_t lds_q[HI * IX_ROW];
   __shared__ __attribute__((aligned(16))) uint8_t lds_k[IX_WAVES][IX_NB][IX_TILE_BYTES];
-  __shared__ float red4[4];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
 

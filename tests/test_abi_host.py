@@ -55,6 +55,12 @@ def test_index_and_topk_validation(lib):
     assert lib.csa_index_scores(*a, 1, 1, 64, 128, 100, 4, 8, 1, None) == CSA_ERR_SHAPE      # unknown flag
     assert lib.csa_topk(P, P, P, None, None, 0, 1, 1, 100, 0, 4, None) == CSA_ERR_SHAPE       # k = 0
     assert lib.csa_topk(P, P, P, None, None, 0, 1, 1, 100, 5000, 4, None) == CSA_ERR_SHAPE    # k > 4096
+    # a row longer than 32 keys per thread is cut into chunks: their kept lists need workspace
+    assert lib.csa_topk_workspace_size(8, 1, 32768, 1024) == 0
+    nws = lib.csa_topk_workspace_size(8, 1, 262144, 1024)
+    assert nws >= 2 * 8 * 16 * 1024 * 8      # 16 chunks of 16384 entries; two buffers of values + indices
+    assert lib.csa_topk(P, P, P, None, None, 0, 8, 1, 262144, 1024, 4, None) == CSA_ERR_WORKSPACE
+    assert lib.csa_topk(P, P, P, None, P, nws - 1, 8, 1, 262144, 1024, 4, None) == CSA_ERR_WORKSPACE
     need = lib.csa_index_topk_workspace_size(2, 1, 100, 16)
     assert need >= 2 * 100 * 4
     assert lib.csa_index_topk(P, P, P, P, P, None, P, need - 1, 2, 1, 64, 128, 100, 16, 4, 0, 1,

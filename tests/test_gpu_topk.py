@@ -1,10 +1,12 @@
 """GPU parity of csa_topk on its own, on fp32 score arrays both sides read
 identically, so the selection must match the oracle exactly: the min(k,
 visible) largest scores, ties to the lower entry index, -1 padding.  Covers
-the three key-storage variants (8 or 32 keys per thread in registers, keys
-re-read from memory), heavy ties across the k-th score, all-equal scores,
-negative and mixed-magnitude values, k larger than the visible range, k = 1
-and the largest k."""
+one-chunk rows (8, 16 or 32 keys per thread), rows cut into chunks whose kept
+lists are selected from again (two and three rounds, chunk edges inside the
+visible range), heavy ties across the k-th score -- also across chunk edges
+--, all-equal scores, negative and mixed-magnitude values, k larger than the
+visible range, k = 1 and the largest k.  The kept entries come out in
+ascending entry order."""
 import numpy as np
 import pytest
 import torch
@@ -35,10 +37,14 @@ CASES = [
     (8192, 1024, [32767, 32767], "ties"),
     (8192, 1, [32767, 100], "wide"),
     (8192, 4096, [32767, 8000], "wide"),
+    (12000, 700, [47999, 40000], "normal"),     # 16 keys per thread
     (20000, 1024, [79999, 50000], "normal"),    # 32 keys per thread
     (20000, 512, [79999], "ties"),
-    (40000, 1024, [159999, 70000], "normal"),   # keys re-read from memory
-    (40000, 2048, [159999], "ties"),
+    (40000, 1024, [159999, 70000], "normal"),   # two rounds, 8192-entry chunks
+    (40000, 2048, [159999, 65539], "ties"),     # two rounds, 16384-entry chunks
+    (262144, 1024, [1048575, 600003], "normal"),
+    (262144, 1024, [1048575], "equal"),         # every chunk ties at the k-th score
+    (300000, 4096, [1199999, 140000], "ties"),  # three rounds
     (5000, 300, [19999, 19999], "equal"),
 ]
 
@@ -54,9 +60,15 @@ def test_topk_matches_oracle(orc, N_cap, k, q_pos, kind):
     o_idx, _ = orc.topk(s64, nvis, k)
     idx = torch.empty((B, S, k), dtype=torch.int32, device="cuda")
     val = torch.empty((B, S, k), dtype=torch.float32, device="cuda")
-    K.csa_topk(torch.from_numpy(s32).cuda(), torch.from_numpy(qp).cuda(), idx, val, ratio=4)
+    nws = K.csa_topk_workspace_size(B, S, N_cap, k)
+    ws = torch.empty(nws, dtype=torch.uint8, device="cuda") if nws else None
+    K.csa_topk(torch.from_numpy(s32).cuda(), torch.from_numpy(qp).cuda(), idx, val, ratio=4, workspace=ws)
     gi = idx.cpu().numpy()
     check_topk_sets(gi, o_idx, s64, nvis, k, exact=True)
+    for row in gi.reshape(-1, k):
+        n = int((row >= 0).sum())
+        assert np.all(row[n:] == -1), "padding follows the kept entries"
+        assert np.all(np.diff(row[:n]) > 0), "kept entries in ascending entry order"
     gv = val.cpu().numpy().reshape(-1, k)
     for qi, row in enumerate(gi.reshape(-1, k)):
         m = row >= 0

@@ -118,8 +118,8 @@ int csa_index_scores(const void* q_idx, const float* w, const void* idx_cache, c
                      csa_stream_t stream);
 
 /*
- * csa_topk -- keeps at most k compressed entries per query, [P5] 2
- * ("保留<=topK个压缩token") and 2.2.
+ * csa_topk -- keeps at most k compressed entries per query, [P5] sections 2
+ * and 2.2.
  *
  * scores: [B, S, N_cap] fp32; only entries e < nvis (same rule as above) are
  *   candidates.  topk_idx: [B, S, k] int32 output: the min(k, nvis) entries

@@ -584,7 +584,10 @@ __global__ __launch_bounds__(512) void attn_tile_kernel(AttnArgs a, int n_hg, in
 template <int NHB>
 __global__ __launch_bounds__(64) void attn_merge_kernel(AttnArgs a, int n_hg, int nsplit,
                                                         const uint8_t* __restrict__ part) {
-  const int qh = blockIdx.x >> 4, wave = (blockIdx.x >> 2) & 3, dt0 = 2 * (blockIdx.x & 3);
+  // the same XCD-aware map as the tile kernel: a (query, head group)'s
+  // partials are read on the XCD whose L2 received them
+  const int mb = xcd_remap(blockIdx.x, (int)gridDim.x);
+  const int qh = mb >> 4, wave = (mb >> 2) & 3, dt0 = 2 * (mb & 3);
   const int qi = qh / n_hg, hgi = qh % n_hg;
   const int lane = threadIdx.x, g = lane >> 4, n = lane & 15;
   const uint8_t* pq = part + (size_t)qh * nsplit * AT_PART_B;

@@ -69,16 +69,17 @@ def algorithmic(sh):
     return per, reads
 
 
-def load_traffic(kernel_call: str, src_hash: str):
-    """HBM traffic per launch from committed rocprofv3 counter runs, if they
-    were taken on the current kernel sources (else None)."""
+def load_traffic(workload: str, kernel_call: str, src_hash: str):
+    """HBM traffic per launch of `kernel_call` in `workload` from committed
+    rocprofv3 counter runs, if they were taken on the current kernel sources
+    (else None)."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     try:
         with open(path) as f:
-            rec = json.load(f).get(kernel_call)
-    except (OSError, ValueError):
+            rec = json.load(f).get("workloads", {}).get(workload, {}).get(kernel_call)
+    except (OSError, ValueError, AttributeError):
         return None
     if not rec or rec.get("src_hash") != src_hash:
         return None
@@ -213,7 +214,7 @@ def main():
     else:
         roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(gbs / HBM_PEAK_GBS, 4)}
-    roof["traffic"] = load_traffic(dominant, src_hash)
+    roof["traffic"] = load_traffic(sh.name, dominant, src_hash)
     roof["kernel"] = dominant
     roof["avg_launch_us"] = round(dom_ms * 1e3, 2)
     roof["algorithmic_bytes_per_launch"] = int(alg_bytes)

@@ -10,15 +10,18 @@
 // so element order is entry order and every load instruction reads 256
 // contiguous bytes.  An MSD radix select over order-preserving 32-bit keys of
 // the fp32 scores finds K*, the k-th largest key, in three digit passes (bits
-// 31..21, 20..10, 9..0).  Every pass counts the keys that still match the
-// digits chosen so far into an LDS histogram (2048 bins; the top digit holds
-// the sign, the exponent and two mantissa bits).  Wave 0 then locates the
-// digit where the count from the top reaches the number of keys still wanted:
-// each lane sums 32 bins, a DPP prefix sum over the lanes finds the lane, and
-// that lane walks its bins; meanwhile the other waves clear the second
-// histogram for the next pass, so a pass costs two barriers.  Kept: every key
-// > K* and the first `remaining` keys == K* in element order; ballots give
-// each kept element its rank, so the output is compact and in entry order.
+// 31..20, 19..9, 8..0).  Every pass counts the keys that still match the
+// digits chosen so far into an LDS histogram (4096, 2048, 512 bins; the top
+// digit holds the sign, the exponent and three mantissa bits, so index scores,
+// which crowd a few binades, still spread over many bins and the LDS atomics
+// collide less).  Wave 0 then locates the digit where the count from the top
+// reaches the number of keys still wanted: each lane sums its 1/64 of the
+// bins, a DPP prefix sum over the lanes finds the lane's range, and a second
+// prefix sum over that range finds the digit; meanwhile the other waves clear
+// the second histogram for the next pass, so a pass costs two barriers.  Kept:
+// every key > K* and the first `remaining` keys == K* in element order;
+// ballots give each kept element its rank, so the output is compact and in
+// entry order.
 //
 // Rows longer than one chunk are cut into chunks whose kept lists (k values
 // and entry indices each, padded with -inf / -1) are concatenated and selected
@@ -43,7 +46,7 @@ __device__ __forceinline__ float key_val(uint32_t key) {  // inverse of ord_key
 
 constexpr int TOPK_THREADS = 1024;
 constexpr int TOPK_WAVES = TOPK_THREADS / 64;
-constexpr int TOPK_BINS = 2048;
+constexpr int TOPK_BINS = 4096;
 
 // Wave 0 only: the digit d (of 64 * PER bins, counted from the top) where the
 // number of keys on digits >= d first reaches `remaining`.  Lane l sums the
@@ -82,20 +85,17 @@ struct TopkShared {
 // Histogram pass over the keys matching `prefix` under `mask`, then wave 0
 // picks the digit while the other waves clear the other histogram.  PASS0:
 // every valid key (key != 0) counts.
-template <int KPT, bool PASS0>
-__device__ __forceinline__ void radix_pass(const uint32_t (&key)[KPT], uint32_t mask, int shift, uint32_t nb,
-                                           uint32_t* h, uint32_t* hn, TopkShared& sh, uint32_t prefix,
-                                           int remaining) {
+template <int KPT, bool PASS0, int NB>
+__device__ __forceinline__ void radix_pass(const uint32_t (&key)[KPT], uint32_t mask, int shift, uint32_t* h,
+                                           uint32_t* hn, TopkShared& sh, uint32_t prefix, int remaining) {
+  constexpr uint32_t nb = NB;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
 #pragma unroll
   for (int j = 0; j < KPT; ++j)
     if (PASS0 ? key[j] != 0u : (key[j] & mask) == prefix) atomicAdd(&h[(key[j] >> shift) & (nb - 1)], 1u);
   __syncthreads();  // histogram complete
   if (wid == 0) {
-    if (nb == 2048)
-      find_digit<32>(h, lane, prefix, shift, remaining, &sh.s_prefix, &sh.s_remaining);
-    else
-      find_digit<16>(h, lane, prefix, shift, remaining, &sh.s_prefix, &sh.s_remaining);
+    find_digit<NB / 64>(h, lane, prefix, shift, remaining, &sh.s_prefix, &sh.s_remaining);
   } else {
     for (int i = tid - 64; i < TOPK_BINS; i += TOPK_THREADS - 64) hn[i] = 0;
   }
@@ -110,13 +110,13 @@ __device__ __forceinline__ void radix_pass(const uint32_t (&key)[KPT], uint32_t 
 template <int KPT>
 __device__ __forceinline__ void radix_kth(const uint32_t (&key)[KPT], int kk, TopkShared& sh, uint32_t* kstar,
                                           int* rem) {
-  radix_pass<KPT, true>(key, 0u, 21, 2048u, sh.hist[0], sh.hist[1], sh, 0u, kk);
+  radix_pass<KPT, true, 4096>(key, 0u, 20, sh.hist[0], sh.hist[1], sh, 0u, kk);
   uint32_t prefix = sh.s_prefix;
   int remaining = sh.s_remaining;
-  radix_pass<KPT, false>(key, 0xffe00000u, 10, 2048u, sh.hist[1], sh.hist[0], sh, prefix, remaining);
+  radix_pass<KPT, false, 2048>(key, 0xfff00000u, 9, sh.hist[1], sh.hist[0], sh, prefix, remaining);
   prefix = sh.s_prefix;
   remaining = sh.s_remaining;
-  radix_pass<KPT, false>(key, 0xfffffc00u, 0, 1024u, sh.hist[0], sh.hist[1], sh, prefix, remaining);
+  radix_pass<KPT, false, 512>(key, 0xfffffe00u, 0, sh.hist[0], sh.hist[1], sh, prefix, remaining);
   *kstar = sh.s_prefix;
   *rem = sh.s_remaining;
 }

@@ -311,18 +311,32 @@ __global__ __launch_bounds__(512) void attn_tile_kernel(AttnArgs a, int n_hg, in
   // slots (padding, out-of-range ids, the ragged tail) point at window row 0
   // and have their bit cleared in the per-tile validity mask.  Dense
   // candidates beyond the table are formed on the fly (all valid).
+  // Every list load is issued first (unconditional, clamped into the list),
+  // then the RoPE table is computed while they are in flight.
   const int nlist = min(ntiles * AT_TR, AT_LIST);
-  for (int j0 = wave * 64; j0 < nlist; j0 += 512) {
+  constexpr int NIT = AT_LIST / 512;  // slot rounds per wave
+  int eid[NIT];
+  const int wpos0 = a.win_pos0 ? a.win_pos0[b] : 0;
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    const int jj = jb0 + wave * 64 + 512 * it + lane - nwin;  // list position of the slot
+    eid[it] = (!a.dense && a.k > 0) ? a.topk_idx[(size_t)qi * a.k + min(max(jj, 0), a.k - 1)] : jj;
+  }
+  fill_rope_table(rope_cs, t, a.rope_dim, a.log2_base, threadIdx.x, 512);
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    const int j0 = wave * 64 + 512 * it;
+    if (j0 >= nlist) break;  // wave-uniform
     const int j = jb0 + j0 + lane;
     int id = -1;
     bool ok = false;
     if (j < nwin) {
       const int u = t - nwin + 1 + j;
-      const int rw = a.win_pos0 ? u - a.win_pos0[b] : u % a.W_cap;
+      const int rw = a.win_pos0 ? u - wpos0 : u % a.W_cap;
       ok = rw >= 0 && rw < a.W_cap;
       id = ok ? -1 - rw : -1;
     } else if (j < ncand) {
-      const int e = a.dense ? j - nwin : a.topk_idx[(size_t)qi * a.k + (j - nwin)];
+      const int e = eid[it];
       ok = e >= 0 && e < a.N_cap;
       id = ok ? e : -1;
     }
@@ -330,7 +344,6 @@ __global__ __launch_bounds__(512) void attn_tile_kernel(AttnArgs a, int n_hg, in
     const uint64_t bal = __builtin_amdgcn_ballot_w64(ok);
     if (lane == 0) s_mask[j0 / AT_TR] = bal;
   }
-  fill_rope_table(rope_cs, t, a.rope_dim, a.log2_base, threadIdx.x, 512);
   // Every ordinary load (and the q copy) is complete here: the compiler then
   // has no pending load to wait for inside the tile loop (such a wait would
   // be vmcnt(0) and drain the copies in flight).

@@ -682,9 +682,9 @@ struct AttnPlan {
   size_t ws_bytes;
 };
 
-static AttnPlan attn_plan(long Q, int H, int n_cand) {
+static AttnPlan attn_plan_nhb(long Q, int H, int n_cand, int nhb) {
   AttnPlan p;
-  p.nhb = (H % 32 == 0) ? 2 : 1;
+  p.nhb = nhb;
   p.n_hg = H / (16 * p.nhb);
   const long items = Q * p.n_hg;
   const int nt = (n_cand + AT_TR - 1) / AT_TR;
@@ -698,6 +698,18 @@ static AttnPlan attn_plan(long Q, int H, int n_cand) {
   p.total = (int)(items * p.nsplit);
   p.ws_bytes = p.nsplit > 1 ? (size_t)p.total * AT_PART_B : 0;
   return p;
+}
+
+// 32 heads per workgroup (each gathered row serves twice the heads per LDS
+// pass), unless that needs more than 4 candidate splits: then 16 heads, so
+// the chip fills with half the splits and the merge reads half the partials
+// (csa_decode_1m, 8 queries: 23.4 -> 19.5 us per call).
+static AttnPlan attn_plan(long Q, int H, int n_cand) {
+  if (H % 32 == 0) {
+    const AttnPlan p2 = attn_plan_nhb(Q, H, n_cand, 2);
+    if (p2.nsplit <= 4) return p2;
+  }
+  return attn_plan_nhb(Q, H, n_cand, 1);
 }
 
 size_t attn_workspace_size(int B, int S, int H, int D, int n_cand) {

@@ -236,6 +236,112 @@ __global__ __launch_bounds__(256) void index_scores_mfma(const bf16* __restrict_
 
 }
 
+// Multi-query form for chunks of positions (S >= 4, prefill): a workgroup of
+// 4 waves scores 4 consecutive queries of one sequence against the same key
+// tiles.  Each 32-row tile is copied once into a 4-slot ring shared by the
+// group (every wave issues a quarter of its copies) and read by all four
+// waves, so the index cache crosses into LDS once per four queries instead of
+// once per query, and with 32 KiB of LDS several groups share a CU.  One
+// barrier per tile: every wave's quarter of tile i has landed, and every wave
+// is done with the slot that the copies of tile i+3 overwrite.  q_idx and w
+// of each wave's query go straight to VGPRs.  Same MFMA tiling, head
+// reduction and score values as index_scores_mfma.
+template <int MT>
+__global__ __launch_bounds__(256) void index_scores_mq(const bf16* __restrict__ q, const float* __restrict__ w,
+                                                       const bf16* __restrict__ K, const int32_t* __restrict__ q_pos,
+                                                       float* __restrict__ scores, int S, int N_cap, int ratio,
+                                                       unsigned flags, int T, int chunks) {
+  constexpr int HI = 16 * MT;
+  constexpr int NB = IX_NB;
+  constexpr int CPW = IX_COPIES / IX_WAVES;  // copies per wave and tile
+  __shared__ __attribute__((aligned(16))) uint8_t lds_k[NB][IX_TILE_BYTES];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15;
+  const int sgroups = (S + IX_WAVES - 1) / IX_WAVES;
+  const int grp = blockIdx.x / chunks, chunk = blockIdx.x % chunks;
+  const int b = grp / sgroups, s0 = (grp % sgroups) * IX_WAVES;
+  const bool live = s0 + wave < S;                // a wave past S scores the last query and stores nothing
+  const int s = min(s0 + wave, S - 1);
+  const int qi = b * S + s;
+  const long tb = (long)q_pos[b];
+  const int nv = (int)visible_entries(tb + s, ratio, N_cap);
+  const int nv_max = (int)visible_entries(tb + min(s0 + IX_WAVES - 1, S - 1), ratio, N_cap);
+  const int e_chunk = chunk * T * IX_TILE;
+  int nt = 0;  // tiles holding candidates visible to some query of the group
+  if (e_chunk < nv_max) nt = min(T, (nv_max - e_chunk + IX_TILE - 1) / IX_TILE);
+  float* out = scores + (size_t)qi * N_cap;
+  const bf16* Kb = K + (size_t)b * N_cap * 128;
+
+  auto issue = [&](int i) {
+    const int e0 = e_chunk + i * IX_TILE;
+#pragma unroll
+    for (int jj = 0; jj < CPW; ++jj) {
+      const int j = CPW * wave + jj;
+      const int r = 4 * j + (lane >> 4);
+      const int c = (lane & 15) ^ (r & 15);
+      int e = e0 + r;
+      e = e < nv_max ? e : nv_max - 1;  // rows past the visible range reload a valid row (masked below)
+      dma16(Kb + (size_t)e * 128 + 8 * c, &lds_k[i % NB][j * 1024]);
+    }
+  };
+  // set-up in one round trip: w and q_idx fragments into VGPRs, the first
+  // NB-1 tiles into LDS
+  float wv[MT][4];
+  bf16x8_t afr[MT][4];
+  const bf16* qb = q + (size_t)qi * HI * 128;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wv[mt][i] = w[(size_t)qi * HI + 16 * mt + 4 * g + i];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) afr[mt][kk] = *(const bf16x8_t*)(qb + (size_t)(16 * mt + n) * 128 + 32 * kk + 8 * g);
+  }
+  for (int i = 0; i < NB - 1 && i < nt; ++i) issue(i);
+  WAIT_VMCNT(0);
+  const bool relu = !(flags & CSA_INDEX_NO_RELU);
+
+  for (int i = 0; i < nt; ++i) {
+    // vector-memory operations issued after tile i's copies: later tiles'
+    // copies and the score stores of tiles max(0, i-NB+1) .. i-1
+    // (a wave past S stores nothing)
+    const int later = min(nt, i + NB - 1) - i - 1;
+    wait_vmcnt_dyn(later * CPW + (live ? min(i, NB - 1) : 0));
+    lds_barrier();                            // tile i complete; slot of tile i-1 free
+    if (i + NB - 1 < nt) issue(i + NB - 1);   // into the slot tile i-1 used
+    const int e0 = e_chunk + i * IX_TILE;
+    const uint8_t* kt = lds_k[i % NB];
+    float mine = -INFINITY;
+#pragma unroll
+    for (int nt2 = 0; nt2 < IX_TILE / 16; ++nt2) {
+      f32x4_t acc[MT];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const bf16x8_t bfr = *(const bf16x8_t*)(kt + (16 * nt2 + n) * IX_ROW + 16 * ((4 * kk + g) ^ n));
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[mt][kk], bfr, acc[mt], 0, 0, 0);
+      }
+      float v = 0.f;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) v += wv[mt][ii] * (relu ? fmaxf(acc[mt][ii], 0.f) : acc[mt][ii]);
+      v = row_sum4(v);
+      if (g == nt2) mine = v;
+    }
+    if (e0 + lane >= nv) mine = -INFINITY;
+    if (live && lane < IX_TILE && e0 + lane < N_cap) out[e0 + lane] = mine;
+  }
+  // the chunk's entries past every query's visible range
+  for (int i = nt; i < T; ++i) {
+    const int e0 = e_chunk + i * IX_TILE;
+    if (e0 >= N_cap) break;
+    if (live && lane < IX_TILE && e0 + lane < N_cap) out[e0 + lane] = -INFINITY;
+  }
+}
+
 }  // namespace csa
 
 namespace csa_host {
@@ -273,6 +379,28 @@ hipError_t launch_index_scores(const void* q, const float* w, const void* K, con
                                int B, int S, int Hi, int di, int N_cap, int ratio, unsigned flags, int dtype,
                                hipStream_t st) {
   const int Q = B * S;
+  if (index_mfma_ok(Hi, di, dtype) && S >= IX_WAVES) {
+    // one workgroup per 4 queries and chunk of T tiles; T such that at least
+    // ~512 workgroups run (two per CU) when the queries alone are fewer
+    const long groups = (long)B * ((S + IX_WAVES - 1) / IX_WAVES);
+    const long tiles = (N_cap + IX_TILE - 1) / IX_TILE;
+    long chunks = (512 + groups - 1) / groups;
+    chunks = chunks > tiles ? tiles : (chunks < 1 ? 1 : chunks);
+    const int T = (int)((tiles + chunks - 1) / chunks);
+    const int nch = (int)((tiles + T - 1) / T);
+    const dim3 grid((unsigned)(groups * nch));
+#define IX_MQ(M)                                                                                                 \
+  hipLaunchKernelGGL((index_scores_mq<M>), grid, dim3(256), 0, st, (const bf16*)q, w, (const bf16*)K, q_pos, scores, \
+                     S, N_cap, ratio, flags, T, nch)
+    switch (Hi / 16) {
+      case 1: IX_MQ(1); break;
+      case 2: IX_MQ(2); break;
+      case 3: IX_MQ(3); break;
+      default: IX_MQ(4); break;
+    }
+#undef IX_MQ
+    return hipGetLastError();
+  }
   if (index_mfma_ok(Hi, di, dtype)) {
     launch_index_mfma<false>(q, w, K, q_pos, scores, Q, S, Hi, N_cap, ratio, flags, FusedCompress{}, st);
     return hipGetLastError();

@@ -76,24 +76,73 @@ __device__ __forceinline__ void compress_load16(const CompressJob& J, int b, lon
   }
 }
 
+constexpr float CMP_LOG2E = 1.4426950408889634f;
+
+// One slot of the online softmax over the slot axis, in the exp2 domain (the
+// running max mx is a score times log2(e); exp2 is one hardware instruction,
+// where expf's library form costs a dozen and makes the C128A pooling, 128
+// slots per channel, VALU-bound).  A missing slot (score -inf) is skipped.
+__device__ __forceinline__ void fold_slot(float sj, float vj, float& mx, float& den, float& num) {
+  if (sj == -INFINITY) return;
+  const float s2 = sj * CMP_LOG2E;
+  if (s2 > mx) {
+    const float r = __builtin_amdgcn_exp2f(mx - s2);
+    den *= r;
+    num *= r;
+    mx = s2;
+  }
+  const float e = __builtin_amdgcn_exp2f(s2 - mx);
+  den += e;
+  num += e * vj;
+}
+
 // Online-softmax fold of 16 loaded slots into (max, denominator, numerator).
 __device__ __forceinline__ void compress_fold16(const PoolRegs& R, float (&mx)[2], float (&den)[2], float (&num)[2]) {
 #pragma unroll
   for (int jj = 0; jj < 16; ++jj)
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const float sj = R.sv[jj][h];
-      if (sj == -INFINITY) continue;
-      if (sj > mx[h]) {
-        const float r = expf(mx[h] - sj);
-        den[h] *= r;
-        num[h] *= r;
-        mx[h] = sj;
-      }
-      const float e = expf(sj - mx[h]);
-      den[h] += e;
-      num[h] += e * R.vv[jj][h];
-    }
+    for (int h = 0; h < 2; ++h) fold_slot(R.sv[jj][h], R.vv[jj][h], mx[h], den[h], num[h]);
+}
+
+// bf16 states, 32 slots j0 .. j0+31 per round trip: the raw bf16 pairs stay
+// packed in registers (one VGPR per slot and tensor) until folded, so a
+// 1024-thread workgroup keeps twice the loads of compress_load16 in flight.
+// Slots >= jend (or missing) are skipped.  Same values and fold order as
+// compress_load16 + compress_fold16 over the same slots.
+__device__ __forceinline__ void compress_fold32_bf16(const CompressJob& J, int b, long g, long p0, int L, int ratio,
+                                                     int p, int j0, int jend, float (&mx)[2], float (&den)[2],
+                                                     float (&num)[2]) {
+  const bf16* __restrict__ kv = (const bf16*)J.kv;
+  const bf16* __restrict__ sc = (const bf16*)J.sc;
+  const int d = J.d, overlap = J.overlap;
+  const size_t row_w = (size_t)(overlap ? 2 : 1) * d;
+  const bf16* kvb = kv + (size_t)b * L * row_w;
+  const bf16* scb = sc + (size_t)b * L * row_w;
+  const int nslot = overlap ? 2 * ratio : ratio;
+  // slot j reads state row r0 + j (both halves of an overlapping state use the
+  // same rows: the previous group's slots are the rows before the group's own)
+  const int r0 = (int)(g * ratio - (overlap ? ratio : 0) - p0);
+  const int jlim = min(nslot, jend);
+  const int first_ok = (overlap && g == 0) ? ratio : 0;  // missing previous group
+  uint32_t kr[32], sr[32];
+  bool ok[32];
+#pragma unroll
+  for (int jj = 0; jj < 32; ++jj) {
+    const int j = j0 + jj;
+    ok[jj] = j < jlim && j >= first_ok;
+    const int ch = (overlap && j >= ratio) ? d + 2 * p : 2 * p;
+    const uint32_t off = (uint32_t)((ok[jj] ? r0 + j : 0) * (int)row_w + ch);
+    kr[jj] = *(const uint32_t*)(kvb + off);
+    sr[jj] = *(const uint32_t*)(scb + off);
+  }
+#pragma unroll
+  for (int jj = 0; jj < 32; ++jj) {
+    if (!ok[jj]) continue;
+    const float sv[2] = {__uint_as_float(sr[jj] << 16), __uint_as_float(sr[jj] & 0xFFFF0000u)};
+    const float vv[2] = {__uint_as_float(kr[jj] << 16), __uint_as_float(kr[jj] & 0xFFFF0000u)};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) fold_slot(sv[h], vv[h], mx[h], den[h], num[h]);
+  }
 }
 
 // Softmax-pooled value (fp32) of channels 2p, 2p+1 of entry g of sequence b
@@ -190,7 +239,13 @@ __device__ __forceinline__ void compress_task_wide(const CompressJob& J, const i
   const int nslot = J.overlap ? 2 * ratio : ratio;
   const int sq = (nslot + 3) / 4;
   float mx[2] = {-INFINITY, -INFINITY}, den[2] = {0.f, 0.f}, num[2] = {0.f, 0.f};
-  if (active) {
+  if constexpr (sizeof(T) == 2) {
+    if (active) {
+      const int jend = min(nslot, (q + 1) * sq);
+      for (int j0 = q * sq; j0 < jend; j0 += 32)
+        compress_fold32_bf16(J, b, g, p0, L, ratio, p, j0, jend, mx, den, num);
+    }
+  } else if (active) {
     for (int j0 = q * sq; j0 < min(nslot, (q + 1) * sq); j0 += 16) {
       PoolRegs R;
       compress_load16<T>(J, b, g, p0, L, ratio, p, j0, R);
@@ -215,12 +270,12 @@ __device__ __forceinline__ void compress_task_wide(const CompressJob& J, const i
       for (int h = 0; h < 2; ++h) {
         if (qm[h] == -INFINITY) continue;  // no slot in this quarter
         if (qm[h] > m2[h]) {
-          const float r = expf(m2[h] - qm[h]);
+          const float r = __builtin_amdgcn_exp2f(m2[h] - qm[h]);
           d2[h] *= r;
           n2[h] *= r;
           m2[h] = qm[h];
         }
-        const float r = expf(qm[h] - m2[h]);
+        const float r = __builtin_amdgcn_exp2f(qm[h] - m2[h]);
         d2[h] += qd[h] * r;
         n2[h] += qn[h] * r;
       }

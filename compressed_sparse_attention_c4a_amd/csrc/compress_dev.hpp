@@ -107,8 +107,8 @@ __device__ __forceinline__ void compress_fold16(const PoolRegs& R, float (&mx)[2
 // bf16 states, 32 slots j0 .. j0+31 per round trip: the raw bf16 pairs stay
 // packed in registers (one VGPR per slot and tensor) until folded, so a
 // 1024-thread workgroup keeps twice the loads of compress_load16 in flight.
-// Slots >= jend (or missing) are skipped.  Same values and fold order as
-// compress_load16 + compress_fold16 over the same slots.
+// Slots >= jend (or missing) are skipped.  The 32 slots are folded as one
+// block (their max, then their exponentials), not slot by slot.
 __device__ __forceinline__ void compress_fold32_bf16(const CompressJob& J, int b, long g, long p0, int L, int ratio,
                                                      int p, int j0, int jend, float (&mx)[2], float (&den)[2],
                                                      float (&num)[2]) {
@@ -135,13 +135,38 @@ __device__ __forceinline__ void compress_fold32_bf16(const CompressJob& J, int b
     kr[jj] = *(const uint32_t*)(kvb + off);
     sr[jj] = *(const uint32_t*)(scb + off);
   }
+  // the chunk's own max first (independent max ops), then its exponentials and
+  // sums in slot order, then one online step into the running state: no
+  // dependency chain through the running max slot by slot
 #pragma unroll
-  for (int jj = 0; jj < 32; ++jj) {
-    if (!ok[jj]) continue;
-    const float sv[2] = {__uint_as_float(sr[jj] << 16), __uint_as_float(sr[jj] & 0xFFFF0000u)};
-    const float vv[2] = {__uint_as_float(kr[jj] << 16), __uint_as_float(kr[jj] & 0xFFFF0000u)};
+  for (int h = 0; h < 2; ++h) {
+    float s2[32];
+    float cm = -INFINITY;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) fold_slot(sv[h], vv[h], mx[h], den[h], num[h]);
+    for (int jj = 0; jj < 32; ++jj) {
+      const uint32_t u = h == 0 ? sr[jj] << 16 : sr[jj] & 0xFFFF0000u;
+      s2[jj] = ok[jj] ? __uint_as_float(u) * CMP_LOG2E : -INFINITY;
+      cm = fmaxf(cm, s2[jj]);
+    }
+    if (cm == -INFINITY) continue;  // no slot in this chunk
+    float cd = 0.f, cn = 0.f;
+#pragma unroll
+    for (int jj = 0; jj < 32; ++jj) {
+      const float e = __builtin_amdgcn_exp2f(s2[jj] - cm);  // 0 for missing slots
+      const uint32_t u = h == 0 ? kr[jj] << 16 : kr[jj] & 0xFFFF0000u;
+      cd += e;
+      cn += e * __uint_as_float(u);
+    }
+    if (cm > mx[h]) {
+      const float r = __builtin_amdgcn_exp2f(mx[h] - cm);
+      den[h] = den[h] * r + cd;
+      num[h] = num[h] * r + cn;
+      mx[h] = cm;
+    } else {
+      const float r = __builtin_amdgcn_exp2f(cm - mx[h]);
+      den[h] += cd * r;
+      num[h] += cn * r;
+    }
   }
 }
 

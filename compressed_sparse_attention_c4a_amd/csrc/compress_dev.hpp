@@ -78,30 +78,42 @@ __device__ __forceinline__ void compress_load16(const CompressJob& J, int b, lon
 
 constexpr float CMP_LOG2E = 1.4426950408889634f;
 
-// One slot of the online softmax over the slot axis, in the exp2 domain (the
-// running max mx is a score times log2(e); exp2 is one hardware instruction,
-// where expf's library form costs a dozen and makes the C128A pooling, 128
-// slots per channel, VALU-bound).  A missing slot (score -inf) is skipped.
-__device__ __forceinline__ void fold_slot(float sj, float vj, float& mx, float& den, float& num) {
-  if (sj == -INFINITY) return;
-  const float s2 = sj * CMP_LOG2E;
-  if (s2 > mx) {
-    const float r = __builtin_amdgcn_exp2f(mx - s2);
-    den *= r;
-    num *= r;
-    mx = s2;
-  }
-  const float e = __builtin_amdgcn_exp2f(s2 - mx);
-  den += e;
-  num += e * vj;
-}
+// The slot softmax runs in the exp2 domain: running maxima are scores times
+// log2(e), and exp2 is one hardware instruction (expf's library form costs a
+// dozen and made the C128A pooling, 128 slots per channel, VALU-bound).
 
-// Online-softmax fold of 16 loaded slots into (max, denominator, numerator).
+// Fold of 16 loaded slots into the running (max, denominator, numerator):
+// the block's own max first, then its exponentials and sums in slot order,
+// then one online step (no dependency chain through the max slot by slot).
 __device__ __forceinline__ void compress_fold16(const PoolRegs& R, float (&mx)[2], float (&den)[2], float (&num)[2]) {
 #pragma unroll
-  for (int jj = 0; jj < 16; ++jj)
+  for (int h = 0; h < 2; ++h) {
+    float s2[16];
+    float cm = -INFINITY;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) fold_slot(R.sv[jj][h], R.vv[jj][h], mx[h], den[h], num[h]);
+    for (int jj = 0; jj < 16; ++jj) {
+      s2[jj] = R.sv[jj][h] * CMP_LOG2E;  // -inf stays -inf
+      cm = fmaxf(cm, s2[jj]);
+    }
+    if (cm == -INFINITY) continue;  // no slot in this block
+    float cd = 0.f, cn = 0.f;
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj) {
+      const float e = __builtin_amdgcn_exp2f(s2[jj] - cm);  // 0 for missing slots
+      cd += e;
+      cn += e * R.vv[jj][h];
+    }
+    if (cm > mx[h]) {
+      const float r = __builtin_amdgcn_exp2f(mx[h] - cm);
+      den[h] = den[h] * r + cd;
+      num[h] = num[h] * r + cn;
+      mx[h] = cm;
+    } else {
+      const float r = __builtin_amdgcn_exp2f(cm - mx[h]);
+      den[h] += cd * r;
+      num[h] += cn * r;
+    }
+  }
 }
 
 // bf16 states, 32 slots j0 .. j0+31 per round trip: the raw bf16 pairs stay

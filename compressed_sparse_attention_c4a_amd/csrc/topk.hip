@@ -55,7 +55,7 @@ constexpr int TOPK_BINS = 4096;
 // that range, from its top, and a second prefix sum finds the digit.
 template <int PER>
 __device__ __forceinline__ void find_digit(const uint32_t* h, int lane, uint32_t prefix, int shift, int remaining,
-                                           uint32_t* s_prefix, int* s_remaining) {
+                                           uint32_t* s_prefix, int* s_remaining, int* s_count) {
   int c = 0;
 #pragma unroll
   for (int i = 0; i < PER / 4; ++i) {
@@ -71,6 +71,7 @@ __device__ __forceinline__ void find_digit(const uint32_t* h, int lane, uint32_t
   if (lane == (int)__builtin_ctzll(__builtin_amdgcn_ballot_w64(lane < PER && incl2 >= remaining))) {
     *s_prefix = prefix | ((uint32_t)d << shift);
     *s_remaining = remaining - (incl2 - hc);
+    *s_count = hc;
   }
 }
 
@@ -80,6 +81,7 @@ struct TopkShared {
   int s_n[TOPK_WAVES];
   uint32_t s_prefix;
   int s_remaining;
+  int s_count;  // keys on the chosen digit
 };
 
 // Histogram pass over the keys matching `prefix` under `mask`, then wave 0
@@ -95,30 +97,41 @@ __device__ __forceinline__ void radix_pass(const uint32_t (&key)[KPT], uint32_t 
     if (PASS0 ? key[j] != 0u : (key[j] & mask) == prefix) atomicAdd(&h[(key[j] >> shift) & (nb - 1)], 1u);
   __syncthreads();  // histogram complete
   if (wid == 0) {
-    find_digit<NB / 64>(h, lane, prefix, shift, remaining, &sh.s_prefix, &sh.s_remaining);
+    find_digit<NB / 64>(h, lane, prefix, shift, remaining, &sh.s_prefix, &sh.s_remaining, &sh.s_count);
   } else {
     for (int i = tid - 64; i < TOPK_BINS; i += TOPK_THREADS - 64) hn[i] = 0;
   }
   __syncthreads();  // digit chosen; next histogram cleared
 }
 
-// K* (the kk-th largest valid key) and how many keys equal to K* are still to
-// be taken; 1 <= kk < number of valid keys.  Invalid slots hold key 0 and
+// K* and `rem` such that the kk largest valid keys are every key > K* plus
+// the first rem keys == K* (K* the kk-th largest key, or just below a digit
+// whose keys are all taken); 1 <= kk < number of valid keys.  Invalid slots hold key 0 and
 // valid keys are >= 2^21, so only the first pass tests validity: every later
 // prefix has a nonzero top digit.  hist[0] must be zero and a barrier passed
 // since it was cleared.  Uniform per workgroup.
 template <int KPT>
 __device__ __forceinline__ void radix_kth(const uint32_t (&key)[KPT], int kk, TopkShared& sh, uint32_t* kstar,
                                           int* rem) {
+  // When every key on the chosen digit is wanted, the keys >= that digit's
+  // lowest key are exactly the kept set: K* is set just below it and no tie
+  // is ranked (later passes skipped).
   radix_pass<KPT, true, 4096>(key, 0u, 20, sh.hist[0], sh.hist[1], sh, 0u, kk);
   uint32_t prefix = sh.s_prefix;
   int remaining = sh.s_remaining;
-  radix_pass<KPT, false, 2048>(key, 0xfff00000u, 9, sh.hist[1], sh.hist[0], sh, prefix, remaining);
-  prefix = sh.s_prefix;
-  remaining = sh.s_remaining;
-  radix_pass<KPT, false, 512>(key, 0xfffffe00u, 0, sh.hist[0], sh.hist[1], sh, prefix, remaining);
-  *kstar = sh.s_prefix;
-  *rem = sh.s_remaining;
+  if (sh.s_count != remaining) {
+    radix_pass<KPT, false, 2048>(key, 0xfff00000u, 9, sh.hist[1], sh.hist[0], sh, prefix, remaining);
+    prefix = sh.s_prefix;
+    remaining = sh.s_remaining;
+    if (sh.s_count != remaining) {
+      radix_pass<KPT, false, 512>(key, 0xfffffe00u, 0, sh.hist[0], sh.hist[1], sh, prefix, remaining);
+      *kstar = sh.s_prefix;
+      *rem = sh.s_remaining;
+      return;
+    }
+  }
+  *kstar = prefix - 1u;  // prefix >= 2^21: valid keys only
+  *rem = 0;
 }
 
 __device__ __forceinline__ int wave_total(int x) {  // sum over the 64 lanes

@@ -158,9 +158,10 @@ __global__ __launch_bounds__(64) void attn_generic_kernel(AttnArgs a) {
 // (split 0).
 //
 // Splits: when there are too few (query, head group) items to fill the chip,
-// an item's tiles are divided between NS workgroups, each of which writes its
-// unnormalised O, running max and sum to the workspace; attn_merge_kernel
-// (launched next on the same stream) combines them at the common maximum.
+// an item's tiles are divided between NS workgroups (16 heads per workgroup
+// when 32 would need more than 4), each of which writes its O divided by its
+// own sum (bf16), its running max and its sum (fp32) to the workspace;
+// attn_merge_kernel (launched next on the same stream) combines them.
 // LDS rows are 1088 bytes apart (64 bytes of padding, no permutation): the
 // row reads of QK^T (ds_read_b128) and the transposed reads of P.V
 // (ds_read_b64_tr_b16) then run at 113-117 B/clk/CU on gfx950, against 95-101
@@ -204,7 +205,7 @@ __device__ __forceinline__ void fill_rope_table(float2* tab, int t, int rope_dim
 
 // Lane (g, n) of dim slice v holds O^T[dim 128*v + 16*dt + 4*g + i][head
 // h0 + 16*hb + n].  The inverse RoPE of position t is a rotation of each tail
-// pair, linear in O: it is applied to unnormalised partial sums as well.
+// pair, linear in O: it is applied before the division by the sum as well.
 template <int NHB>
 __device__ __forceinline__ void derotate(f32x4_t (&o)[8][NHB], int v, int lane, int rope_dim,
                                          const float2* rope_cs) {

@@ -36,10 +36,15 @@ WORKLOADS = {
 
 
 def _kernel_sources_hash(files):
+    """Hash of the kernel sources with // comments and blank lines removed, so
+    that counter records stay valid across comment-only edits."""
     h = hashlib.sha256()
     for f in files:
-        with open(os.path.join(ROOT, "compressed_sparse_attention_c4a_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "compressed_sparse_attention_c4a_amd", "csrc", f), encoding="utf-8") as fh:
+            for line in fh:
+                code = line.split("//", 1)[0].rstrip()
+                if code:
+                    h.update(code.encode("utf-8") + b"\n")
     return h.hexdigest()[:16]
 
 

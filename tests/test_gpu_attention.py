@@ -48,7 +48,8 @@ def _dev(a):
 
 VARIANTS = {
     # name: (B, S, H, N_cap, W_cap, k, q_pos, linear window, window)
-    # 32 heads per workgroup, 2 splits (sparse) / 6 splits, most of them empty (dense)
+    # 32 heads per workgroup, 2 splits (sparse) / 16 heads, 6 splits, most of them empty (dense:
+    # 32 heads would need more than 4 splits)
     "split_decode_short_ctx": (5, 1, 128, 600, 128, 96, [2399, 1000, 130, 7, 0], False, 128),
     # 256 (query, head group) items: no split
     "nosplit_decode": (64, 1, 128, 300, 128, 40, list(range(400, 1040, 10)), False, 128),
@@ -56,7 +57,7 @@ VARIANTS = {
     # 16 heads per workgroup (H % 32 != 0)
     "h48_groups_of_16": (3, 1, 48, 100, 64, 33, [399, 250, 60], False, 64),
     "h96_window_gt_ctx": (100, 1, 96, 64, 128, 20, list(range(0, 200, 2)), False, 128),
-    # largest list and window: 48 tiles in 16 splits of 3
+    # largest list and window: 48 tiles in 16 splits of 3 (16 heads per workgroup)
     "max_list_16_splits": (2, 1, 32, 4096, 1024, 2048, [16383, 9000], False, 1024),
     # 16 heads, one item, 6 splits
     "h16_one_item_splits": (1, 1, 16, 2000, 256, 512, [7999], False, 256),

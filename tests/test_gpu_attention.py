@@ -51,6 +51,8 @@ VARIANTS = {
     # 32 heads per workgroup, 2 splits (sparse) / 16 heads, 6 splits, most of them empty (dense:
     # 32 heads would need more than 4 splits)
     "split_decode_short_ctx": (5, 1, 128, 600, 128, 96, [2399, 1000, 130, 7, 0], False, 128),
+    # 32 heads per workgroup at the split limit: 64 items, 4 splits
+    "h128_four_splits": (16, 1, 128, 2000, 128, 512, list(range(7999, 7999 - 16 * 37, -37)), False, 128),
     # 256 (query, head group) items: no split
     "nosplit_decode": (64, 1, 128, 300, 128, 40, list(range(400, 1040, 10)), False, 128),
     "prefill_linear_window": (1, 160, 128, 200, 160 + 127, 48, [600], True, 128),

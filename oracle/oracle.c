@@ -38,10 +38,14 @@
  *     window rows and compressed entries form one candidate set; the same row
  *     serves as key and value.
  *
- * Parity unpinned: none of the functions below (each has a CPU test that
- * pins it against closed forms, invariants, library routines or the worked
- * value printed in [P1]); the model-fidelity constants listed above are
- * readings, not pinned values.
+ * Pins (CPU tests): every function below is checked against closed forms,
+ * invariants, library routines, brute force or the worked value printed in
+ * [P1], for fp32/fp64 inputs and for bf16 inputs (known bit patterns widen to
+ * their IEEE values; bf16-coded inputs give the same results as the same
+ * values in fp64), and a mutation run plants mistakes in copies of this file
+ * and checks that a pin fails for each.  Parity unpinned: only the
+ * model-fidelity constants listed above, which are readings of the pages,
+ * not values the pages fix.
  */
 #include <math.h>
 #include <stdint.h>

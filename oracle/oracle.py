@@ -10,7 +10,9 @@ Sources: "DeepSeek-V4-Pro 架构：一个 token 的旅程" (hs-black.github.io) 
 function follows.
 
 Input arrays may be float32, float64, or uint16 holding bf16 bit patterns;
-they are widened exactly inside the C code.  Outputs are float64.
+they are widened exactly inside the C code.  Outputs are float64.  Fresh
+cache entries are stored in the cache's own type: bf16 caches receive the
+fp64 value rounded once to nearest-even bf16 (round_bf16).
 """
 from __future__ import annotations
 
@@ -222,9 +224,35 @@ def _rope_mat(x, pos, rope_dim, base, sign):
     return x
 
 
+def _bf16_exact(x: float) -> float:
+    """x rounded to the nearest bf16 value (8 significant bits, exponent down
+    to -126, then subnormals of spacing 2^-133), ties to the even significand,
+    in exact rational arithmetic.  Finite inputs below 2^128 only."""
+    from fractions import Fraction
+    a = abs(Fraction(x))
+    if a == 0:
+        return float(x)
+    e = a.numerator.bit_length() - a.denominator.bit_length()   # 2^e <= a < 2^(e+2)
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    ulp = Fraction(2) ** (max(e, -126) - 7)
+    q = a / ulp
+    n = q.numerator // q.denominator
+    rest = q - n
+    if rest > Fraction(1, 2) or (rest == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    y = float(n * ulp)
+    return -y if x < 0 else y
+
+
 def dense_pipeline(inp: dict) -> dict:
     """Whole CSA (or HCA when inp['hca']) path for sequences that start at
-    position 0 and are queried causally at every token, via dense masks."""
+    position 0 and are queried causally at every token, via dense masks.
+    With inp['store'] == 'bf16' the compressed entries are rounded to bf16
+    (nearest, ties to even) before the indexer and the attention read them,
+    as a bf16 cache stores them."""
     kv = _f64(inp["kv_state"])          # [B, T, m*d]
     sc = _f64(inp["score_state"])
     B, T, md = kv.shape
@@ -253,7 +281,12 @@ def dense_pipeline(inp: dict) -> dict:
             out[:, g] = _rope_mat(y, np.full((B,), g * ratio), rope_dim, base, +1)
         return out
 
-    cache = entries(kv, sc, d, inp["gamma"], rope_dim)
+    def store(vals):
+        if inp.get("store") != "bf16":
+            return vals
+        return np.vectorize(_bf16_exact, otypes=[np.float64])(vals)
+
+    cache = store(entries(kv, sc, d, inp["gamma"], rope_dim))
     q = _f64(inp["q"])                 # [B, T, H, D]
     win = _f64(inp["win_kv"])          # [B, T, D] linear rows for positions 0..T-1
     H = q.shape[2]
@@ -264,7 +297,7 @@ def dense_pipeline(inp: dict) -> dict:
     if not inp.get("hca", False):
         ikv, isc = _f64(inp["idx_kv_state"]), _f64(inp["idx_score_state"])
         di = ikv.shape[-1] // 2
-        icache = entries(ikv, isc, di, inp["idx_gamma"], inp["idx_rope_dim"])
+        icache = store(entries(ikv, isc, di, inp["idx_gamma"], inp["idx_rope_dim"]))
         qi = _f64(inp["q_idx"])        # [B, T, Hi, di]
         w = np.asarray(inp["w"], dtype=np.float64)       # [B, T, Hi]
         dots = np.einsum("bthc,bgc->bthg", qi, icache)
@@ -301,15 +334,34 @@ def dense_pipeline(inp: dict) -> dict:
 # --------------------------------------------------------------------------
 # Stage composition (C oracle)
 # --------------------------------------------------------------------------
+def round_bf16(values64) -> np.ndarray:
+    """bf16 bit patterns (uint16) of fp64 values, rounded once to the nearest
+    bf16 value, ties to the even significand (IEEE round-to-nearest-even).
+
+    bf16 keeps 8 significant bits.  A value with frexp exponent E (|x| in
+    [2^(E-1), 2^E)) has bf16 spacing 2^(E-8); below the smallest normal 2^-126
+    the spacing stays 2^-133 (subnormals).  Scaling by a power of two is
+    exact, numpy's round() takes ties to even, and the rounded value has at
+    most 8 significant bits, so its float32 form is exact and its upper 16
+    bits are the bf16 pattern (a carry past 2^128 gives infinity)."""
+    x = np.asarray(values64, dtype=np.float64)
+    _, E = np.frexp(x)
+    E = np.maximum(E, -125)
+    y = np.ldexp(np.round(np.ldexp(x, 8 - E)), E - 8)
+    with np.errstate(over="ignore"):
+        y32 = y.astype(np.float32)
+    return (y32.view(np.uint32) >> 16).astype(np.uint16)
+
+
 def _store_like(raw: np.ndarray, values64: np.ndarray) -> np.ndarray:
-    """Round fp64 values to the storage type of ``raw`` (bf16 bits: via fp32,
-    nearest-even; fp32: nearest)."""
-    f = np.asarray(values64, dtype=np.float64).astype(np.float32)
+    """Round fp64 values once to the storage type of ``raw``: bf16 bits by
+    round_bf16, fp32 by numpy's nearest-even cast, fp64 unchanged.  The caches
+    are bf16 in the bf16 configurations, so the attention and index stages
+    read entries rounded this way."""
     if raw.dtype == np.uint16:
-        u = f.view(np.uint32)
-        return ((u + ((u >> 16) & 1) + np.uint32(0x7FFF)) >> 16).astype(np.uint16)
+        return round_bf16(values64)
     if raw.dtype == np.float32:
-        return f
+        return np.asarray(values64, dtype=np.float64).astype(np.float32)
     return np.asarray(values64, dtype=np.float64)
 
 

@@ -88,14 +88,18 @@ __device__ __forceinline__ void wait_vmcnt_dyn(int n) {
   }
 }
 
-// Fused compressors (decode, FUSED): the wave whose tile holds the index-key
+// Fused compressors (decode, FUSED): the wave whose tile holds an index-key
 // entry this step writes computes that entry itself (the compressor's own
 // routines, so the same values) and puts it into its LDS tile before scoring
 // it: no workgroup waits for the compressor.  The entries are written to the
 // caches by the top-k launch that follows (topk.hip).  Requires S == 1, an
 // overlapping index-key compressor and a state of at most 2*ratio <= 16
-// tokens: then at most one index-key entry per sequence is written, with at
-// most 16 slots.
+// tokens, so every entry has at most 16 slots.  Such a state completes one
+// entry g > 0 at most (it needs all 2*ratio tokens); only a state that starts
+// at position 0 also completes entry 0, which has no previous group.  Entries
+// 0 and 1 are rows 0 and 1 of the first tile of the first chunk, so one wave
+// holds both: the later entry is computed when its tile is scored, as usual;
+// the other (this rare case only) is computed during the set-up.
 template <int MT, bool FUSED>
 __global__ __launch_bounds__(256) void index_scores_mfma(const bf16* __restrict__ q, const float* __restrict__ w,
                                                          const bf16* __restrict__ K,
@@ -163,10 +167,14 @@ __global__ __launch_bounds__(256) void index_scores_mfma(const bf16* __restrict_
     // Fused: the index-key entry written this step, if it is visible and in
     // one of this wave's tiles (tile pi, row pr): its slots are loaded now,
     // its value is computed when that tile is scored.
-    [[maybe_unused]] int pi = -1, pr = 0;
+    // (pi2, pr2): a second entry of this wave (entry 0 of a state that starts
+    // at position 0), its stored pair pv2 computed here.
+    [[maybe_unused]] int pi = -1, pr = 0, pi2 = -1, pr2 = 0;
     [[maybe_unused]] long pg = 0;
+    [[maybe_unused]] uint32_t pv2 = 0;
     [[maybe_unused]] PoolRegs pregs;
     if constexpr (FUSED) {
+      long pg2 = 0;
       for (int x = 0; x < F.gx; ++x) {
         const long ge = compress_group(F.j1, pp0, x, F.L, ratio);
         if (ge < 0 || ge >= nv) continue;
@@ -174,9 +182,23 @@ __global__ __launch_bounds__(256) void index_scores_mfma(const bf16* __restrict_
         if (rel < 0 || rel >= (long)IX_WAVES * T * IX_TILE) continue;
         const int tg = (int)(rel / IX_TILE);
         if (tg % IX_WAVES != wave) continue;
+        if (pi >= 0) {  // keep the earlier entry as the second one
+          pi2 = pi;
+          pr2 = pr;
+          pg2 = pg;
+        }
         pi = tg / IX_WAVES;
         pr = (int)(rel % IX_TILE);
         pg = ge;
+      }
+      if (pi2 >= 0) {
+        PoolRegs r2;
+        compress_load16<bf16>(F.j1, b, pg2, pp0, F.L, ratio, lane, 0, r2);
+        const float2 y = compress_pool16(r2);
+        const float tot = wave_sum(y.x * y.x + y.y * y.y);
+        const float2 v = compress_finish(F.j1, y, tot, pg2, ratio, F.eps, F.log2_base, lane, F.j1.gamma[2 * lane],
+                                         F.j1.gamma[2 * lane + 1]);
+        pv2 = (uint32_t)f2bf(v.x) | ((uint32_t)f2bf(v.y) << 16);
       }
       if (pi >= 0) compress_load16<bf16>(F.j1, b, pg, pp0, F.L, ratio, lane, 0, pregs);
     }
@@ -202,6 +224,8 @@ __global__ __launch_bounds__(256) void index_scores_mfma(const bf16* __restrict_
         wait_vmcnt_dyn(later * IX_COPIES + min(i, IX_NB - 1));
         const uint8_t* kt = lds_k[wave][i % IX_NB];
         if constexpr (FUSED) {
+          if (i == pi2)
+            *(uint32_t*)(lds_k[wave][i % IX_NB] + pr2 * IX_ROW + 16 * ((lane >> 2) ^ (pr2 & 15)) + 4 * (lane & 3)) = pv2;
           if (i == pi) {  // this step's entry replaces whatever the copy brought
             const float2 y = compress_pool16(pregs);
             const float tot = wave_sum(y.x * y.x + y.y * y.y);

@@ -2,7 +2,10 @@
 
 Tolerances (stated once, used everywhere):
   * floating-point outputs: normwise relative error max|gpu - ref| / max|ref|
-    <= 1e-2 for bf16 outputs and <= 1e-4 for fp32 outputs;
+    <= 1e-2 for bf16 outputs and <= 1e-4 for fp32 outputs; every comparison
+    also records the rms-scaled error max|gpu - ref| / rms(ref) and the
+    elementwise relative error max |gpu - ref| / max(|ref|, 1e-3 rms(ref)),
+    printed per case and summarised at the end of the session;
   * index-score buffers (fp32 outputs of bf16 or fp32 inputs): <= 1e-3 for
     bf16 inputs (bf16 products are exact in fp32; the bound covers fp32
     accumulation order) and <= 1e-4 for fp32 inputs;
@@ -37,6 +40,35 @@ def raw_np(t: torch.Tensor) -> np.ndarray:
     return t.numpy()
 
 
+def elementwise(gpu, ref, floor=1e-3) -> float:
+    """max_i |gpu_i - ref_i| / max(|ref_i|, floor * rms(ref)): the relative
+    error of every element, with a floor for elements near zero."""
+    gpu = np.asarray(gpu, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    if ref.size == 0:
+        return 0.0
+    rms = float(np.sqrt(np.mean(ref * ref)))
+    den = np.maximum(np.abs(ref), floor * rms)
+    den = np.where(den > 0, den, 1.0)
+    return float(np.max(np.abs(gpu - ref) / den))
+
+
+def rmswise(gpu, ref) -> float:
+    """max_i |gpu_i - ref_i| / rms(ref): the largest error on the scale of a
+    typical element (stricter than the normwise form by max|ref| / rms)."""
+    gpu = np.asarray(gpu, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    if ref.size == 0:
+        return 0.0
+    rms = float(np.sqrt(np.mean(ref * ref)))
+    d = float(np.max(np.abs(gpu - ref)))
+    return d / rms if rms > 0 else d
+
+
+# (what, normwise, rms-scaled, elementwise) of every comparison made in this session
+REPORT = []
+
+
 def normwise(gpu, ref) -> float:
     gpu = np.asarray(gpu, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
@@ -45,8 +77,13 @@ def normwise(gpu, ref) -> float:
 
 
 def assert_close(gpu, ref, tol, what):
+    """Asserts the normwise bar; also records and prints the rms-scaled and
+    the elementwise error of the same comparison."""
     assert np.all(np.isfinite(gpu)), f"{what}: non-finite GPU values"
     err = normwise(gpu, ref)
+    rw, el = rmswise(gpu, ref), elementwise(gpu, ref)
+    REPORT.append((what, err, rw, el))
+    print(f"[parity] {what}: normwise {err:.3e} rms-scaled {rw:.3e} elementwise {el:.3e}", flush=True)
     assert err <= tol, f"{what}: normwise relative error {err:.3e} > {tol:.1e}"
     return err
 

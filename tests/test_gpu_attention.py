@@ -63,6 +63,8 @@ VARIANTS = {
     "max_list_16_splits": (2, 1, 32, 4096, 1024, 2048, [16383, 9000], False, 1024),
     # 16 heads, one item, 6 splits
     "h16_one_item_splits": (1, 1, 16, 2000, 256, 512, [7999], False, 256),
+    # 256 items, no split, dense lists of 3100-3200 entries: candidates past the 3072-slot table
+    "dense_past_table_nosplit": (64, 1, 128, 3200, 128, 16, [12399 + 7 * i for i in range(64)], False, 128),
 }
 
 

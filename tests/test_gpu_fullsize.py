@@ -2,17 +2,17 @@
 bench times (the same Step: every library call of one pass, same shapes).
 
 Decode workloads compare every output with the oracle.  The prefill chunk
-(8192 queries) compares every compressed row it writes, and a sample of
-queries -- the first ones, group boundaries, the last ones -- that the oracle
-recomputes one by one (index scores, top-k set, attention on the GPU's own
-selection)."""
+(8192 queries) compares every compressed row it writes, and 256 sampled
+queries (runs of 8 consecutive positions: the first, the last and 30 spread
+at random) whose full score rows, top-k sets and outputs (attention on the
+GPU's own selection) the oracle recomputes."""
 import numpy as np
 import pytest
 import torch
 
 from compressed_sparse_attention_c4a_amd import path as P
 from compressed_sparse_attention_c4a_amd import workloads as W
-from parity import TOL, assert_close, check_topk_sets, to_np
+from parity import SCORE_TOL, TOL, assert_close, check_topk_sets, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -55,7 +55,21 @@ def test_decode_full_size(orc, name):
     assert_close(step.lse.cpu().numpy(), l2, 1e-3, f"{name}: lse")
 
 
+def _prefill_sample(S, runs=32, run_len=8, seed=0):
+    """Starts of `runs` runs of `run_len` consecutive queries: the first and
+    the last run of the chunk and the rest spread at random.  A run of 8
+    covers every position mod 8, so every group phase (t mod 4) and both
+    sides of every group boundary; runs start at multiples of 8, the query
+    groups of the multi-query indexer."""
+    rng = np.random.default_rng(seed)
+    mid = rng.choice(np.arange(1, S // run_len - 1), size=runs - 2, replace=False) * run_len
+    return sorted([0, S - run_len] + mid.tolist())
+
+
 def test_prefill_chunk_sampled_queries(orc):
+    """The 8192-query prefill chunk: every cache row it writes, and 256
+    queries (32 runs of 8) whose full score rows, top-k sets and outputs the
+    oracle recomputes."""
     sh = W.csa_prefill_32k()
     inp = W.generate(sh)
     print(f"[fullsize] prefill: S={sh.S} after {sh.q_pos}", flush=True)
@@ -69,12 +83,22 @@ def test_prefill_chunk_sampled_queries(orc):
                                            inp["idx_gamma"], inp["state_pos0"], sh.ratio, True, sh.idx_rope)
     assert_close(_rows(dev["idx_cache"], iw), ivals[iw], TOL["bf16"], "prefill: index-key rows")
     gi_all = step.topk_idx.cpu().numpy()
-    for s in (0, 1, 2, 3, 4, 1023, 4094, 4095, 8190, 8191):
-        qp = np.asarray([sh.q_pos + s], dtype=np.int32)
-        sc, nvis = orc.index_scores(inp["q_idx"][:, s:s + 1], inp["w"][:, s:s + 1], idx_new, qp, sh.ratio)
+    # the score buffer at the start of the workspace: [B, S, N_cap] fp32
+    scores_all = step.idx_ws[:4 * sh.B * sh.S * sh.N_cap].view(torch.float32).view(sh.B, sh.S, sh.N_cap)
+    L = 8
+    starts = _prefill_sample(sh.S, runs=32, run_len=L)
+    print(f"[fullsize] prefill: runs of {L} queries at {starts}", flush=True)
+    for s0 in starts:
+        sl = slice(s0, s0 + L)
+        qp = np.asarray([sh.q_pos + s0], dtype=np.int32)
+        sc, nvis = orc.index_scores(inp["q_idx"][:, sl], inp["w"][:, sl], idx_new, qp, sh.ratio)
+        got = scores_all[:, sl].cpu().numpy().astype(np.float64)
+        vis = np.isfinite(sc)
+        np.testing.assert_array_equal(np.isfinite(got), vis)      # visibility is exact
+        assert_close(got[vis], sc[vis], SCORE_TOL["bf16"], f"prefill: score rows {s0}..{s0 + L - 1}")
         o_idx, _ = orc.topk(sc, nvis, sh.k)
-        gi = gi_all[:, s:s + 1]
+        gi = gi_all[:, sl]
         check_topk_sets(gi, o_idx, sc, nvis, sh.k)
-        o2, _, _ = orc.attn(inp["q"][:, s:s + 1], cmp_new, inp["win_kv"], inp["sink"], qp, topk_idx=gi,
+        o2, _, _ = orc.attn(inp["q"][:, sl], cmp_new, inp["win_kv"], inp["sink"], qp, topk_idx=gi,
                             ratio=sh.ratio, win_pos0=inp["win_pos0"], window=sh.window, rope_dim=sh.rope)
-        assert_close(to_np(out[:, s:s + 1]), o2, TOL["bf16"], f"prefill: output of query {s}")
+        assert_close(to_np(out[:, sl]), o2, TOL["bf16"], f"prefill: outputs of queries {s0}..{s0 + L - 1}")

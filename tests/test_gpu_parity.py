@@ -144,14 +144,17 @@ def test_fused_compress_index_topk_equals_separate_calls(case):
 def test_fused_decode_new_entry_at_tile_and_chunk_edges():
     """Decode at full N_cap with the freshly written index entry at the
     first/last row of a wave tile, of a workgroup chunk and of the cache: the
-    wave that scores it computes it in the fused launch."""
-    entries = [0, 31, 32, 255, 256, 4095, 5000, 8191]
+    wave that scores it computes it in the fused launch.  Entry 1 (position 7,
+    state starting at position 0) completes entries 0 and 1 in the same step:
+    both must be scored from their new values."""
+    entries = [0, 1, 31, 32, 255, 256, 4095, 5000, 8191]
     q_pos = [4 * e + 3 for e in entries]
     sh = W.Shape(name="csa_decode_edges", B=len(entries), S=1, N_cap=8192, window=128, W_cap=128, state_len=8,
                  k=1024, seed=21)
     inp = dict(W.generate(sh))
     inp["q_pos"] = np.asarray(q_pos, dtype=np.int32)
     inp["state_pos0"] = (inp["q_pos"] - 7).astype(np.int32)
+    assert inp["state_pos0"][1] == 0
     print(f"[fused] entries {entries}", flush=True)
     _assert_fused_equal(inp)
 

@@ -49,8 +49,12 @@ def _kernel_sources_hash(files):
 
 
 def algorithmic(sh):
-    """Algorithmic bytes and flops per QUERY of each call (what the method must
-    move or compute; re-reads and temporary score buffers are excluded)."""
+    """Algorithmic bytes and flops per QUERY of each call: what the method
+    must move or compute.  Re-reads and the temporary score buffer are
+    excluded: with one position per sequence (decode) every gathered row is a
+    distinct read; with a chunk of positions (prefill) each sequence's
+    compressed and window rows count once for the whole chunk (consecutive
+    queries share them), q, out, q_idx, w and the index lists once per query."""
     e = 2 if sh.dtype == "bf16" else 4
     t_last = sh.q_pos + sh.S - 1
     nvis = min((t_last + 1) // sh.ratio, sh.N_cap)
@@ -59,19 +63,47 @@ def algorithmic(sh):
     groups = max(1, sh.S // sh.ratio) if sh.S > 1 else 1
     per = {}
     cmp = {"bytes": (2 * sh.state_len * m * sh.D * e + groups * sh.D * e) / sh.S, "flops": 0.0}
+    # rows of the window span of the chunk (decode: the window itself)
+    win_rows = min(sh.S + sh.window - 1, t_last + 1) if sh.S > 1 else nwin
     if sh.indexer:  # both compressors, the index scores and the top-k in one call
         cmp["bytes"] += (2 * sh.state_len * 2 * sh.di * e + groups * sh.di * e) / sh.S
+        nvis_avg = np.mean([min((sh.q_pos + s + 1) // sh.ratio, sh.N_cap) for s in range(sh.S)])
         per["compress_index_topk"] = {
-            "bytes": cmp["bytes"] + nvis * sh.di * e + sh.Hi * sh.di * e + sh.Hi * 4 + sh.k * 4,
-            "flops": 2.0 * sh.Hi * sh.di * nvis}
+            "bytes": cmp["bytes"] + nvis * sh.di * e / sh.S + sh.Hi * sh.di * e + sh.Hi * 4 + sh.k * 4,
+            "flops": 2.0 * sh.Hi * sh.di * nvis_avg}
         reads = nwin + min(sh.k, nvis)
-        per["attn"] = {"bytes": reads * sh.D * e + 2 * sh.H * sh.D * e + sh.k * 4,
+        rows = (win_rows + min(sh.N_cap, nvis if sh.S > 1 else min(sh.k, nvis))) / sh.S if sh.S > 1 else reads
+        per["attn"] = {"bytes": rows * sh.D * e + 2 * sh.H * sh.D * e + sh.k * 4,
                        "flops": 4.0 * sh.H * reads * sh.D}
     else:
         per["compress"] = cmp
         reads = nwin + nvis
-        per["attn"] = {"bytes": reads * sh.D * e + 2 * sh.H * sh.D * e, "flops": 4.0 * sh.H * reads * sh.D}
+        rows = (win_rows + nvis) / sh.S if sh.S > 1 else reads
+        per["attn"] = {"bytes": rows * sh.D * e + 2 * sh.H * sh.D * e, "flops": 4.0 * sh.H * reads * sh.D}
     return per, reads
+
+
+def roofline_of(alg_bytes, alg_flops, seconds):
+    """The bound (whichever of HBM and MFMA time is larger), what was
+    achieved against it, and the fraction of its peak."""
+    gbs = alg_bytes / seconds / 1e9
+    tfl = alg_flops / seconds / 1e12
+    if alg_flops / (MFMA_BF16_PEAK_TFLOPS * 1e12) > alg_bytes / (HBM_PEAK_GBS * 1e9):
+        return {"bound": "mfma", "achieved": round(tfl, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(tfl / MFMA_BF16_PEAK_TFLOPS, 4)}
+    return {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4)}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def load_traffic(workload: str, kernel_call: str, src_hash: str):
@@ -107,6 +139,7 @@ def cpu_baseline(inp, seconds: float):
             break
     q = reps * sh.B * sh.S
     return {"value": q / dt, "unit": "queries/s", "cores": O.num_threads(), "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"{reps} full passes (compress, index scores, top-k, attention; fp64) over the whole batch of "
                       f"{sh.name} ({sh.B * sh.S} queries each), {dt:.1f} s wall"}
 
@@ -152,10 +185,15 @@ def main():
     sh = getattr(W, WORKLOADS[args.workload])()
     inp = W.generate(sh)
     dev0 = P.to_device(inp, "cuda")
-    # bytes one copy of the inputs occupies; rotate enough copies to exceed 2x the 256 MB MALL
+    # rotate enough input copies that the bytes one step touches, summed over
+    # the copies, exceed 4x the 256 MB Infinity Cache (bounded by memory)
+    per, reads = algorithmic(sh)
+    touched = sum(p["bytes"] for p in per.values()) * sh.B * sh.S
+    if sh.indexer:
+        touched += 4.0 * sh.B * sh.S * sh.N_cap            # the score buffer
     copy_bytes = sum(v.numel() * v.element_size() for k, v in dev0.items() if k != "shape" and v is not None)
-    R = args.rotate or max(2, int(np.ceil(2 * 256e6 / copy_bytes)) + 1)
-    R = min(R, 64)
+    R = args.rotate or max(2, int(np.ceil(4 * 256e6 / touched)) + 1)
+    R = max(1, min(R, 64, int(100e9 // copy_bytes)))
     devs = [dev0] + [{k: (v.clone() if (k != "shape" and v is not None) else v) for k, v in dev0.items()}
                      for _ in range(R - 1)]
     steps = [P.Step(d) for d in devs]
@@ -163,7 +201,6 @@ def main():
     # every library call of a step marshalled once per input copy
     prepared = [st.calls(d, stream, prepare=True) for st, d in zip(steps, devs)]
 
-    per, reads = algorithmic(sh)
     calls = list(per)
     Q = sh.B * sh.S
 
@@ -209,16 +246,7 @@ def main():
     src_hash = _kernel_sources_hash(src)
     alg_bytes = per[dominant]["bytes"] * Q
     alg_flops = per[dominant]["flops"] * Q
-    gbs = alg_bytes / (dom_ms * 1e-3) / 1e9
-    tfl = alg_flops / (dom_ms * 1e-3) / 1e12
-    hbm_t = alg_bytes / (HBM_PEAK_GBS * 1e9)
-    mfma_t = alg_flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)
-    if mfma_t > hbm_t:
-        roof = {"bound": "mfma", "achieved": round(tfl, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(tfl / MFMA_BF16_PEAK_TFLOPS, 4)}
-    else:
-        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    roof = roofline_of(alg_bytes, alg_flops, dom_ms * 1e-3)
     roof["traffic"] = load_traffic(sh.name, dominant, src_hash)
     roof["kernel"] = dominant
     roof["avg_launch_us"] = round(dom_ms * 1e3, 2)
@@ -226,8 +254,15 @@ def main():
     roof["algorithmic_flops_per_launch"] = int(alg_flops)
 
     step_bytes = sum(p["bytes"] for p in per.values()) * Q
-    whole = {"bytes_per_step": int(step_bytes), "hbm_roofline_step_us": round(step_bytes / (HBM_PEAK_GBS * 1e9) * 1e6, 2),
-             "frac_of_hbm_roofline": round(step_bytes / (HBM_PEAK_GBS * 1e9) / (ms_per_step * 1e-3), 4)}
+    step_flops = sum(p["flops"] for p in per.values()) * Q
+    step_roof_s = max(step_bytes / (HBM_PEAK_GBS * 1e9), step_flops / (MFMA_BF16_PEAK_TFLOPS * 1e12))
+    whole = {"bytes_per_step": int(step_bytes), "flops_per_step": int(step_flops),
+             "bound": "mfma" if step_flops / (MFMA_BF16_PEAK_TFLOPS * 1e12) > step_bytes / (HBM_PEAK_GBS * 1e9)
+             else "hbm",
+             "roofline_step_us": round(step_roof_s * 1e6, 2),
+             "frac_of_roofline": round(step_roof_s / (ms_per_step * 1e-3), 4),
+             "per_call": {c: roofline_of(per[c]["bytes"] * Q, per[c]["flops"] * Q, avg_probe[c] * 1e-3)
+                          for c in calls}}
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -129,6 +129,23 @@ __device__ __forceinline__ void dma16_sbase(const void* sbase, uint32_t lane_off
 // [6:4] = 7, lgkmcnt [11:8] = 15, vmcnt[5:4] in [15:14]).
 #define WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt((((n)&15) | (((n) >> 4) << 14)) | 0x0F70)
 
+// s_waitcnt vmcnt(n) for a run-time n in [0, 30] (the count is an immediate;
+// larger n waits for everything).
+__device__ __forceinline__ void wait_vmcnt_dyn(int n) {
+  switch (n) {
+#define IX_W(k) \
+  case k:       \
+    WAIT_VMCNT(k); \
+    break;
+    IX_W(0) IX_W(1) IX_W(2) IX_W(3) IX_W(4) IX_W(5) IX_W(6) IX_W(7) IX_W(8) IX_W(9) IX_W(10) IX_W(11) IX_W(12)
+    IX_W(13) IX_W(14) IX_W(15) IX_W(16) IX_W(17) IX_W(18) IX_W(19) IX_W(20) IX_W(21) IX_W(22) IX_W(23) IX_W(24)
+    IX_W(25) IX_W(26) IX_W(27) IX_W(28) IX_W(29) IX_W(30)
+#undef IX_W
+    default:
+      WAIT_VMCNT(0);
+  }
+}
+
 // Workgroup barrier for LDS traffic only: this wave's LDS reads/writes are
 // complete (lgkmcnt 0) and the compiler may not move memory accesses across
 // it.  Copies in flight are not waited for (explicit vmcnt waits track them);

@@ -72,22 +72,6 @@ constexpr int IX_COPIES = IX_TILE_BYTES / 1024;  // 1 KiB copies per tile and wa
 #define IX_MQW 8                      // queries (waves) per workgroup of the multi-query form
 #endif
 
-// s_waitcnt vmcnt(n) for a run-time n in [0, 31] (the count is an immediate).
-__device__ __forceinline__ void wait_vmcnt_dyn(int n) {
-  switch (n) {
-#define IX_W(k) \
-  case k:       \
-    WAIT_VMCNT(k); \
-    break;
-    IX_W(0) IX_W(1) IX_W(2) IX_W(3) IX_W(4) IX_W(5) IX_W(6) IX_W(7) IX_W(8) IX_W(9) IX_W(10) IX_W(11) IX_W(12)
-    IX_W(13) IX_W(14) IX_W(15) IX_W(16) IX_W(17) IX_W(18) IX_W(19) IX_W(20) IX_W(21) IX_W(22) IX_W(23) IX_W(24)
-    IX_W(25) IX_W(26) IX_W(27) IX_W(28) IX_W(29) IX_W(30)
-#undef IX_W
-    default:
-      WAIT_VMCNT(0);
-  }
-}
-
 // Fused compressors (decode, FUSED): the wave whose tile holds an index-key
 // entry this step writes computes that entry itself (the compressor's own
 // routines, so the same values) and puts it into its LDS tile before scoring

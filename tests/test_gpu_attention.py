@@ -94,22 +94,35 @@ def test_attention_variants(orc, name, dense):
     assert_close(lse.cpu().numpy(), rlse, 1e-3, f"{name} dense={dense}: lse")
 
 
-def test_sparse_with_every_visible_entry_equals_dense():
+def test_sparse_with_every_visible_entry_equals_dense(orc):
     B, S, H, N_cap = 4, 1, 128, 256
-    x = _inputs(7, B, S, H, N_cap, 128, 256, [1023, 700, 300, 40])
-    topk = np.full((B, S, 256), -1, dtype=np.int32)
-    for b in range(B):
-        nv = min((int(x["q_pos"][b]) + 1) // 4, N_cap)
-        topk[b, 0, :nv] = np.arange(nv)
-    o1 = torch.empty((B, S, H, 512), dtype=torch.bfloat16, device="cuda")
-    o2 = torch.empty_like(o1)
-    K.csa_sparse_attn(_dev(x["q"]), _dev(x["cmp"]), _dev(topk), _dev(x["win"]), None, _dev(x["sink"]),
-                      _dev(x["q_pos"]), o1, rope_dim=64, window=128)
-    K.hca_attn(_dev(x["q"]), _dev(x["cmp"]), _dev(x["win"]), None, _dev(x["sink"]), _dev(x["q_pos"]), o2, ratio=4,
-               rope_dim=64, window=128)
-    # same candidates in the same order, and k == N_cap gives both calls the
-    # same split of the list: the two must agree bit for bit
+
+    def both(q_pos):
+        x = _inputs(7, B, S, H, N_cap, 128, 256, q_pos)
+        topk = np.full((B, S, 256), -1, dtype=np.int32)
+        for b in range(B):
+            nv = min((int(x["q_pos"][b]) + 1) // 4, N_cap)
+            topk[b, 0, :nv] = np.arange(nv)
+        o1 = torch.empty((B, S, H, 512), dtype=torch.bfloat16, device="cuda")
+        o2 = torch.empty_like(o1)
+        K.csa_sparse_attn(_dev(x["q"]), _dev(x["cmp"]), _dev(topk), _dev(x["win"]), None, _dev(x["sink"]),
+                          _dev(x["q_pos"]), o1, rope_dim=64, window=128)
+        K.hca_attn(_dev(x["q"]), _dev(x["cmp"]), _dev(x["win"]), None, _dev(x["sink"]), _dev(x["q_pos"]), o2,
+                   ratio=4, rope_dim=64, window=128)
+        return x, topk, o1, o2
+
+    # every entry visible (k == N_cap == visible): the two calls see the same
+    # candidates in the same slots and the same split of them, so they agree
+    # bit for bit
+    _, _, o1, o2 = both([1023, 2000, 1500, 4000])
     assert torch.equal(o1, o2)
+    # fewer visible entries than k: the sparse list is padded with -1, the
+    # slots differ, the values agree within the bar
+    x, topk, o1, o2 = both([1023, 700, 300, 40])
+    ref, _, _ = orc.attn(x["q"], x["cmp"], x["win"], x["sink"], x["q_pos"], topk_idx=None, ratio=4, window=128,
+                         rope_dim=64)
+    assert_close(to_np(o1), ref, TOL["bf16"], "sparse over every visible entry")
+    assert_close(to_np(o2), ref, TOL["bf16"], "dense")
 
 
 @pytest.mark.parametrize("B,H,N_cap,k,q_pos", [(2, 64, 50, 16, [199, 150]), (1, 32, 2000, 1024, [7000])])

@@ -46,6 +46,8 @@ def load() -> ctypes.CDLL:
         "csa_index_topk": ([vp, vp, vp, vp, vp, vp, vp, sz, i32, i32, i32, i32, i32, i32, i32, u32, i32, vp], i32),
         "csa_compress_index_topk": ([vp, vp, vp, vp, i32, i32, i32, vp, vp, vp, vp, i32, vp, i32, vp, vp, vp, vp, vp,
                                      vp, sz, i32, i32, i32, i32, i32, i32, i32, u32, f32, f32, i32, vp], i32),
+        "csa_compress_index_topk_noalloc": ([vp, vp, vp, vp, i32, i32, i32, vp, vp, vp, vp, i32, vp, i32, vp, vp, vp,
+                                             vp, vp, i32, i32, i32, i32, i32, i32, i32, u32, f32, f32, i32, vp], i32),
         "csa_attn_workspace_size": ([i32, i32, i32, i32, i32], sz),
         "csa_sparse_attn": ([vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i32, i32, i32, i32, i32, i32, i32, i32, i32,
                              f32, f32, i32, vp], i32),
@@ -213,7 +215,8 @@ def csa_compress_index_topk(kv_state, score_state, gamma, cache, idx_kv_state, i
                             rope_dim: int, idx_rope_dim: int, workspace, relu: bool = True, eps: float = 1e-6,
                             rope_base: float = 10000.0, stream=None, prepare: bool = False):
     """csa_compress_kv_index followed by csa_index_topk over idx_cache, one
-    call (one fused launch plus top-k for decode)."""
+    call (one fused launch plus top-k for decode).  workspace=None calls
+    csa_compress_index_topk_noalloc (the library's static scratch)."""
     B, L, md = kv_state.shape
     d, di = cache.shape[-1], idx_cache.shape[-1]
     _, S, Hi, qdi = q_idx.shape
@@ -226,16 +229,18 @@ def csa_compress_index_topk(kv_state, score_state, gamma, cache, idx_kv_state, i
     if qdi != di or cache.shape[1] != N_cap:
         raise ValueError("q_idx dims must equal the index cache's, and both caches must hold N_cap entries")
     dt = kv_state.dtype
-    ws_bytes = workspace.numel() * workspace.element_size()
-    args = (_ptr(kv_state, dt, "kv_state"), _ptr(score_state, dt, "score_state"), _ptr(gamma, torch.float32, "gamma"),
+    head = (_ptr(kv_state, dt, "kv_state"), _ptr(score_state, dt, "score_state"), _ptr(gamma, torch.float32, "gamma"),
             _ptr(cache, dt, "cache"), d, rope_dim, int(overlap), _ptr(idx_kv_state, dt, "idx_kv_state"),
             _ptr(idx_score_state, dt, "idx_score_state"), _ptr(idx_gamma, torch.float32, "idx_gamma"),
             _ptr(idx_cache, dt, "idx_cache"), idx_rope_dim, _ptr(state_pos0, torch.int32, "state_pos0"), L,
             _ptr(q_idx, dt, "q_idx"), _ptr(w, torch.float32, "w"), _ptr(q_pos, torch.int32, "q_pos"),
-            _ptr(topk_idx, torch.int32, "topk_idx"), _ptr(topk_score, torch.float32, "topk_score"),
-            _ptr(workspace, None, "workspace"), ws_bytes, B, S, Hi, di, N_cap, k, ratio,
-            0 if relu else CSA_INDEX_NO_RELU, eps, rope_base, _dtype_code(kv_state), _stream(stream))
-    return _run("csa_compress_index_topk", args, prepare)
+            _ptr(topk_idx, torch.int32, "topk_idx"), _ptr(topk_score, torch.float32, "topk_score"))
+    tail = (B, S, Hi, di, N_cap, k, ratio, 0 if relu else CSA_INDEX_NO_RELU, eps, rope_base, _dtype_code(kv_state),
+            _stream(stream))
+    if workspace is None:
+        return _run("csa_compress_index_topk_noalloc", head + tail, prepare)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    return _run("csa_compress_index_topk", head + (_ptr(workspace, None, "workspace"), ws_bytes) + tail, prepare)
 
 
 def csa_attn_workspace_size(B: int, S: int, H: int, D: int, n_cand: int) -> int:

@@ -7,6 +7,13 @@
 #include "common.hpp"
 
 #include <cmath>
+#include <mutex>
+
+// Scratch of csa_compress_index_topk_noalloc: one copy per GPU, resolved to
+// a device address once per device (the array's name is a host-side stand-in
+// in host code: only the address returned by hipGetSymbolAddress is passed to
+// kernels).
+static __device__ __align__(256) uint8_t scratch[CSA_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -230,6 +237,53 @@ int csa_index_topk(const void* q_idx, const float* w, const void* idx_cache, con
   if (e != hipSuccess) return launched(fn, e);
   return launched(fn, csa_host::launch_topk(scores, q_pos, topk_idx, topk_score, tws, B, S, N_cap, k, ratio,
                                             (hipStream_t)stream));
+}
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (resolved on the first
+// call on that device).
+int scratch_address(const char* fn, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(CSA_ERR_HIP, "%s: hipGetDevice failed: %s", fn, hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(CSA_ERR_UNSUPPORTED, "%s: device %d out of range", fn, dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(CSA_ERR_HIP, "%s: hipGetSymbolAddress of the scratch array failed: %s", fn, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return CSA_OK;
+}
+}  // namespace
+
+int csa_compress_index_topk_noalloc(const void* kv_state, const void* score_state, const float* gamma, void* cache,
+                                    int d, int rope_dim, int overlap, const void* idx_kv_state,
+                                    const void* idx_score_state, const float* idx_gamma, void* idx_cache,
+                                    int idx_rope_dim, const int32_t* state_pos0, int L, const void* q_idx,
+                                    const float* w, const int32_t* q_pos, int32_t* topk_idx, float* topk_score, int B,
+                                    int S, int Hi, int di, int N_cap, int k, int ratio, unsigned flags, float eps,
+                                    float rope_base, int dtype, csa_stream_t stream) {
+  const char* fn = "csa_compress_index_topk_noalloc";
+  if (B < 1 || S < 1 || N_cap < 1 || k < 1)
+    return fail(CSA_ERR_SHAPE, "%s: B, S, N_cap and k must be >= 1", fn);
+  const size_t need = csa_index_topk_workspace_size(B, S, N_cap, k);
+  if (need > CSA_NOALLOC_SCRATCH_BYTES)
+    return fail(CSA_ERR_WORKSPACE, "%s: %zu bytes of scratch needed, the static array holds %zu", fn, need,
+                (size_t)CSA_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if (int rc = scratch_address(fn, &ws)) return rc;
+  return csa_compress_index_topk(kv_state, score_state, gamma, cache, d, rope_dim, overlap, idx_kv_state,
+                                 idx_score_state, idx_gamma, idx_cache, idx_rope_dim, state_pos0, L, q_idx, w, q_pos,
+                                 topk_idx, topk_score, ws, need, B, S, Hi, di, N_cap, k, ratio, flags, eps, rope_base,
+                                 dtype, stream);
 }
 
 int csa_compress_index_topk(const void* kv_state, const void* score_state, const float* gamma, void* cache, int d,

@@ -166,6 +166,32 @@ int csa_compress_index_topk(const void* kv_state, const void* score_state, const
                             csa_stream_t stream);
 
 /*
+ * csa_compress_index_topk_noalloc -- csa_compress_index_topk without a
+ * workspace argument, for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  The score buffer and the top-k round buffers live in a static
+ * device array of the library, CSA_NOALLOC_SCRATCH_BYTES on every GPU the
+ * library runs on (held until the process ends).  Arguments, results and
+ * launches are those of csa_compress_index_topk; the scores are not
+ * returned.  The first call on a device resolves the array's address on that
+ * device (hipGetSymbolAddress, done once per device: make that first call
+ * outside graph capture); no call allocates or frees anything.  Every call on
+ * one GPU uses the same array: calls that may overlap in time on one GPU
+ * (different streams without ordering) race.  Returns CSA_ERR_WORKSPACE when
+ * csa_index_topk_workspace_size(B, S, N_cap, k) exceeds
+ * CSA_NOALLOC_SCRATCH_BYTES (decode up to B * N_cap = 16M entries; longer
+ * prefill chunks need the workspace form).
+ */
+#define CSA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int csa_compress_index_topk_noalloc(const void* kv_state, const void* score_state, const float* gamma, void* cache,
+                                    int d, int rope_dim, int overlap, const void* idx_kv_state,
+                                    const void* idx_score_state, const float* idx_gamma, void* idx_cache,
+                                    int idx_rope_dim, const int32_t* state_pos0, int L, const void* q_idx,
+                                    const float* w, const int32_t* q_pos, int32_t* topk_idx, float* topk_score, int B,
+                                    int S, int Hi, int di, int N_cap, int k, int ratio, unsigned flags, float eps,
+                                    float rope_base, int dtype, csa_stream_t stream);
+
+/*
  * csa_sparse_attn -- multi-query attention over the window plus the selected
  * compressed entries, [P1] "局部和压缩记忆，共用一次归一化" (one candidate set, one
  * softmax, per-head sink adds to the denominator only), "输出投影也分组…"

@@ -32,6 +32,8 @@ WORKLOADS = {
     "csa_prefill_8k_at_24k": "csa_prefill_32k",
     "hca_decode_128k": "hca_decode_128k",
     "csa_decode_1m": "csa_decode_1m",
+    "hca_decode_32k": "hca_decode_32k",
+    "swa_decode_32k": "swa_decode_32k",
 }
 
 
@@ -62,6 +64,10 @@ def algorithmic(sh):
     m = 2 if sh.overlap else 1
     groups = max(1, sh.S // sh.ratio) if sh.S > 1 else 1
     per = {}
+    if sh.swa:  # window rows, q and out only
+        win_rows = min(sh.S + sh.window - 1, t_last + 1) if sh.S > 1 else nwin
+        per["attn"] = {"bytes": win_rows / sh.S * sh.D * e + 2 * sh.H * sh.D * e, "flops": 4.0 * sh.H * nwin * sh.D}
+        return per, nwin
     cmp = {"bytes": (2 * sh.state_len * m * sh.D * e + groups * sh.D * e) / sh.S, "flops": 0.0}
     # rows of the window span of the chunk (decode: the window itself)
     win_rows = min(sh.S + sh.window - 1, t_last + 1) if sh.S > 1 else nwin

@@ -53,6 +53,7 @@ def load() -> ctypes.CDLL:
                              f32, f32, i32, vp], i32),
         "hca_attn": ([vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i32, i32, i32, i32, i32, i32, i32, i32, i32, f32, f32,
                       i32, vp], i32),
+        "swa_attn": ([vp, vp, vp, vp, vp, vp, vp, vp, sz, i32, i32, i32, i32, i32, i32, i32, f32, f32, i32, vp], i32),
     }
     for name, (args, res) in sigs.items():
         fn = getattr(L, name)
@@ -288,3 +289,21 @@ def hca_attn(q, cmp_cache, win_kv, win_pos0, sink, q_pos, out, lse=None, *, rati
             _ptr(out, q.dtype, "out"), _ptr(lse, torch.float32, "lse"), _ptr(workspace, None, "workspace"), ws_bytes,
             B, S, H, D, rope_dim, N_cap, ratio, W_cap, window, scale, rope_base, _dtype_code(q), _stream(stream))
     return _run("hca_attn", args, prepare, keep=(workspace,))
+
+
+def swa_attn(q, win_kv, win_pos0, sink, q_pos, out, lse=None, *, rope_dim: int, window: int,
+             softmax_scale: Optional[float] = None, rope_base: float = 10000.0, workspace=None, stream=None,
+             prepare: bool = False):
+    """Sliding-window attention layer: the window rows, the sink and the
+    inverse RoPE, no compressed channel."""
+    B, S, H, D = q.shape
+    W_cap = win_kv.shape[1]
+    scale = softmax_scale if softmax_scale is not None else D ** -0.5
+    if workspace is None:
+        workspace = attn_workspace(B, S, H, D, window, q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    args = (_ptr(q, q.dtype, "q"), _ptr(win_kv, q.dtype, "win_kv"), _ptr(win_pos0, torch.int32, "win_pos0"),
+            _ptr(sink, torch.float32, "sink"), _ptr(q_pos, torch.int32, "q_pos"), _ptr(out, q.dtype, "out"),
+            _ptr(lse, torch.float32, "lse"), _ptr(workspace, None, "workspace"), ws_bytes, B, S, H, D, rope_dim, W_cap,
+            window, scale, rope_base, _dtype_code(q), _stream(stream))
+    return _run("swa_attn", args, prepare, keep=(workspace,))

@@ -383,4 +383,20 @@ int hca_attn(const void* q, const void* cmp_cache, const void* win_kv, const int
                                             rope_base, dtype, (hipStream_t)stream));
 }
 
+int swa_attn(const void* q, const void* win_kv, const int32_t* win_pos0, const float* sink, const int32_t* q_pos,
+             void* out, float* lse, void* workspace, size_t workspace_bytes, int B, int S, int H, int D, int rope_dim,
+             int W_cap, int window, float softmax_scale, float rope_base, int dtype, csa_stream_t stream) {
+  const char* fn = "swa_attn";
+  if (int rc = check_attn_common(fn, q, nullptr, win_kv, win_pos0, sink, q_pos, out, lse, B, S, H, D, rope_dim, 0,
+                                 W_cap, window, dtype))
+    return rc;
+  const size_t need = csa_host::attn_workspace_size(B, S, H, D, window);
+  if (need && (!workspace || workspace_bytes < need))
+    return fail(CSA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed (got %zu)", fn, need, workspace_bytes);
+  OPT_PTR(workspace);
+  return launched(fn, csa_host::launch_attn(q, nullptr, nullptr, 0, 0, 1, win_kv, win_pos0, sink, q_pos, out, lse,
+                                            workspace, B, S, H, D, rope_dim, 0, W_cap, window, softmax_scale,
+                                            rope_base, dtype, (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -41,7 +41,9 @@ class Step:
         device = q.device
         self.out = torch.empty_like(q)
         self.lse = torch.empty((sh.B, sh.S, sh.H), dtype=torch.float32, device=device)
-        if sh.indexer:
+        if sh.swa:
+            n_cand = sh.window
+        elif sh.indexer:
             self.topk_idx = torch.empty((sh.B, sh.S, sh.k), dtype=torch.int32, device=device)
             ws = K.csa_index_topk_workspace_size(sh.B, sh.S, sh.N_cap, sh.k)
             self.idx_ws = torch.empty(max(ws, 1), dtype=torch.uint8, device=device)
@@ -62,6 +64,10 @@ class Step:
                 return fn(*a, **kw, **P)
             return lambda: fn(*a, **kw, stream=stream)
 
+        if sh.swa:
+            # sliding-window layer: the window rows, the sink and the inverse RoPE only
+            return [("attn", thunk(K.swa_attn, dev["q"], dev["win_kv"], dev.get("win_pos0"), dev["sink"], dev["q_pos"],
+                                   self.out, self.lse, rope_dim=sh.rope, window=sh.window, workspace=self.attn_ws))]
         if sh.indexer:
             # both compressors (main KV and index keys), index scores and top-k
             c = [("compress_index_topk",
@@ -101,3 +107,26 @@ class Step:
             else:
                 fn()
         return self.out
+
+
+class LayerStack:
+    """One decode pass through a stack of attention layers, each of its own
+    type (CSA, HCA or SWA; see schedule.attention_kinds) with its own caches
+    and inputs.  The Q/O projections between layers are outside this path, so
+    every layer's q is its own generated input."""
+
+    def __init__(self, devs: list):
+        self.devs = devs
+        self.steps = [Step(d) for d in devs]
+
+    def calls(self, stream=None, prepare: bool = False):
+        out = []
+        for i, (st, d) in enumerate(zip(self.steps, self.devs)):
+            for name, fn in st.calls(d, stream, prepare=prepare):
+                out.append((f"layer{i}.{d['shape'].kind}.{name}", fn))
+        return out
+
+    def run(self, stream=None):
+        for _, fn in self.calls(stream):
+            fn()
+        return [st.out for st in self.steps]

@@ -85,6 +85,7 @@ class Shape:
     state_pos0: int = 0       # absolute position of compressor state row 0
     state_len: int = 8
     indexer: bool = True
+    swa: bool = False         # sliding-window layer: no compressed channel at all
     Hi: int = 64
     di: int = 128
     idx_rope: int = 64
@@ -99,6 +100,10 @@ class Shape:
     @property
     def queries(self) -> int:
         return self.B * self.S
+
+    @property
+    def kind(self) -> str:
+        return "swa" if self.swa else ("csa" if self.indexer else "hca")
 
 
 def generate(sh: Shape, seed: Optional[int] = None) -> dict:
@@ -183,6 +188,38 @@ def hca_decode_128k(B: int = 64) -> Shape:
     t = 131071
     return Shape(name="hca_decode_128k", B=B, S=1, q_pos=t, ratio=128, overlap=False, N_cap=1024, n_pre=1023,
                  window=128, W_cap=128, state_pos0=t - 127, state_len=128, indexer=False, seed=3)
+
+
+def hca_decode_32k(B: int = 32) -> Shape:
+    """HCA decode at 32K: 256 entries, the last written by this step."""
+    t = 32767
+    return Shape(name="hca_decode_32k", B=B, S=1, q_pos=t, ratio=128, overlap=False, N_cap=256, n_pre=255,
+                 window=128, W_cap=128, state_pos0=t - 127, state_len=128, indexer=False, seed=5)
+
+
+def swa_decode_32k(B: int = 32) -> Shape:
+    """Sliding-window layer at 32K: the 128 window rows only (no compressed
+    cache, no compressor)."""
+    t = 32767
+    return Shape(name="swa_decode_32k", B=B, S=1, q_pos=t, ratio=1, overlap=False, N_cap=0, n_pre=0, window=128,
+                 W_cap=128, state_pos0=t, state_len=0, indexer=False, swa=True, seed=6)
+
+
+def layer_shape(kind: str, B: int, t: int, seed: int) -> Shape:
+    """Shape of one decode layer of the given attention type at position t
+    (sizes of the Pro model; small contexts give small caches)."""
+    if kind == "csa":
+        n = (t + 1) // 4
+        return Shape(name=f"csa_t{t}", B=B, S=1, q_pos=t, N_cap=n, n_pre=n - 1, state_pos0=t - 7, state_len=8,
+                     k=min(1024, max(n, 1)), seed=seed)
+    if kind == "hca":
+        n = max((t + 1) // 128, 1)
+        return Shape(name=f"hca_t{t}", B=B, S=1, q_pos=t, ratio=128, overlap=False, N_cap=n, n_pre=n - 1,
+                     state_pos0=t - 127, state_len=128, indexer=False, seed=seed)
+    if kind == "swa":
+        return Shape(name=f"swa_t{t}", B=B, S=1, q_pos=t, ratio=1, overlap=False, N_cap=0, state_pos0=t,
+                     state_len=0, indexer=False, swa=True, seed=seed)
+    raise ValueError(f"unknown attention type {kind}")
 
 
 def csa_decode_1m(B: int = 8) -> Shape:

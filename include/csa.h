@@ -238,6 +238,19 @@ int hca_attn(const void* q, const void* cmp_cache, const void* win_kv, const int
              int H, int D, int rope_dim, int N_cap, int ratio, int W_cap, int window, float softmax_scale,
              float rope_base, int dtype, csa_stream_t stream);
 
+/*
+ * swa_attn -- sliding-window attention layer ([P5] 1: the model's third
+ * attention type, SWA): multi-query attention over the window rows alone,
+ * with the per-head sink and the inverse RoPE of csa_sparse_attn ([P1]
+ * "局部和压缩记忆，共用一次归一化", "输出投影也分组…"; [P5] 2 window ring, 2.3).
+ * Arguments and results are those of csa_sparse_attn without a compressed
+ * channel (no cache, no list: N_cap = k = 0); workspace:
+ * csa_attn_workspace_size(B, S, H, D, window).
+ */
+int swa_attn(const void* q, const void* win_kv, const int32_t* win_pos0, const float* sink, const int32_t* q_pos,
+             void* out, float* lse, void* workspace, size_t workspace_bytes, int B, int S, int H, int D, int rope_dim,
+             int W_cap, int window, float softmax_scale, float rope_base, int dtype, csa_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -386,6 +386,16 @@ def pipeline(inp: dict, eps: float = 1e-6, rope_base: float = 10000.0, topk_over
     module): compress -> [index scores -> top-k] -> attention."""
     sh = inp["shape"]
     res = {}
+    if getattr(sh, "swa", False):
+        # sliding-window layer ("图解DeepSeek V4" 1: SWA): the window rows only,
+        # with the sink and the inverse RoPE; no compressed channel
+        q = inp["q"]
+        none = np.zeros((sh.B, 0, q.shape[-1]), dtype=q.dtype)
+        out, lse, ncand = attn(q, none, inp["win_kv"], inp["sink"], inp["q_pos"],
+                               topk_idx=np.zeros((sh.B, sh.S, 0), dtype=np.int32), ratio=1,
+                               win_pos0=inp.get("win_pos0"), window=sh.window, rope_dim=sh.rope, rope_base=rope_base)
+        res["out"], res["lse"], res["ncand"] = out, lse, ncand
+        return res
     cmp_new, written, vals = compress_into(inp["cmp_cache"], inp["kv_state"], inp["score_state"], inp["gamma"],
                                            inp["state_pos0"], sh.ratio, sh.overlap, sh.rope, eps, rope_base)
     res["cmp_cache"], res["written"], res["cmp_vals"] = cmp_new, written, vals

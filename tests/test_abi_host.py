@@ -108,6 +108,17 @@ def test_attention_validation(lib):
                         1, None) == CSA_ERR_SHAPE               # ratio 0
 
 
+def test_swa_validation(lib):
+    def swa(q=P, win=P, sink=P, qp=P, out=P, B=2, H=128, D=512, rope=64, W=128, window=128, dtype=1, ws=None, nws=0):
+        return lib.swa_attn(q, win, None, sink, qp, out, None, ws, nws, B, 1, H, D, rope, W, window, 0.04, 10000.0,
+                            dtype, None)
+    assert swa(win=None) == CSA_ERR_NULL
+    assert swa(q=MIS) == CSA_ERR_ALIGN
+    assert swa(window=129) == CSA_ERR_SHAPE
+    assert swa(dtype=3) == CSA_ERR_DTYPE
+    assert swa(B=8, H=16, W=1024, window=1024) == CSA_ERR_WORKSPACE   # 8 items over 16 tiles: split partials
+
+
 def test_binding_refuses_host_tensors():
     import torch
     x = torch.zeros(4)

@@ -415,3 +415,66 @@ def pipeline(inp: dict, eps: float = 1e-6, rope_base: float = 10000.0, topk_over
                            rope_base=rope_base)
     res["out"], res["lse"], res["ncand"] = out, lse, ncand
     return res
+
+
+# --------------------------------------------------------------------------
+# Projections around the attention ("DeepSeek-V4-Pro 架构：一个 token 的旅程")
+# --------------------------------------------------------------------------
+def _rows_pos(pos, M: int, S: int) -> np.ndarray:
+    """Position of each of the M = B*S rows: row m is token m % S of sequence
+    m // S, whose first token sits at pos[m // S]."""
+    pos = np.asarray(pos, dtype=np.int64).reshape(-1)
+    m = np.arange(M)
+    return pos[m // S] + m % S
+
+
+def q_proj(x, wq_a, gamma_q, wq_b, pos, *, H: int, D: int, rope_dim: int, S: int = 1, eps: float = 1e-6,
+           rope_base: float = 10000.0, store=None):
+    """Low-rank query, section "低秩 Q：两次矩阵乘法接起来".
+
+    x [M, d_model] (M = B*S rows), wq_a [q_rank, d_model], gamma_q [q_rank],
+    wq_b [H*D, q_rank], pos [B].  In order:
+      qr = RMSNorm(x wq_a^T) with gain gamma_q (the page writes rms_norm);
+      q  = qr wq_b^T viewed as [M, H, D];
+      every head divided by sqrt(mean over its D dims of q^2 + eps);
+      RoPE on the last rope_dim dims at the row's position (the same pair
+      rotation as the compressed entries).
+    store == 'bf16' rounds qr once to bf16 before the second product, the
+    precision in which it is held between the two matrix products.
+    Returns (q [M, H, D], qr [M, q_rank]) in fp64."""
+    X = _f64(x)
+    M = X.shape[0]
+    qr = X @ _f64(wq_a).T
+    qr = qr / np.sqrt(np.mean(qr * qr, axis=-1, keepdims=True) + eps) * _f64(gamma_q)[None, :]
+    if store == "bf16":
+        qr = _f64(round_bf16(qr))
+    q = (qr @ _f64(wq_b).T).reshape(M, H, D)
+    q = q / np.sqrt(np.mean(q * q, axis=-1, keepdims=True) + eps)
+    t = _rows_pos(pos, M, S)
+    for m in range(M):
+        for h in range(H):
+            q[m, h, D - rope_dim:] = rope(q[m, h, D - rope_dim:], float(t[m]), rope_base)
+    return q, qr
+
+
+def o_proj(o, wo_a, wo_b, *, groups: int, store=None):
+    """Grouped output projection, section "输出投影也分组，并且降低中间维度".
+
+    o [M, H, D] is the attention output with the inverse RoPE already applied
+    (the attention stage does it).  Heads h = 8g .. 8g+7 (H/groups of them,
+    in order) form group g, whose H*D/groups inputs are projected by its own
+    wo_a[g] [o_rank, H*D/groups]; the groups*o_rank results, group-major, are
+    projected by wo_b [d_model, groups*o_rank].
+    store == 'bf16' rounds r once to bf16 before the second product.
+    Returns (y [M, d_model], r [M, groups, o_rank]) in fp64."""
+    O = _f64(o)
+    M = O.shape[0]
+    Wa = _f64(wo_a)
+    og = O.reshape(M, groups, -1)
+    r = np.empty((M, groups, Wa.shape[1]), dtype=np.float64)
+    for g in range(groups):
+        r[:, g, :] = og[:, g, :] @ Wa[g].T
+    if store == "bf16":
+        r = _f64(round_bf16(r))
+    y = r.reshape(M, -1) @ _f64(wo_b).T
+    return y, r

@@ -15,7 +15,7 @@ from concurrent.futures import ThreadPoolExecutor
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-PINS = ["tests/test_oracle_pins.py", "tests/test_oracle_bf16_pins.py"]
+PINS = ["tests/test_oracle_pins.py", "tests/test_oracle_bf16_pins.py", "tests/test_oracle_proj_pins.py"]
 
 # (name, file, original text, mutated text): the original must occur in the file
 MUTANTS = [
@@ -48,7 +48,27 @@ MUTANTS = [
      "    x = np.asarray(values64, dtype=np.float64).astype(np.float32).astype(np.float64)\n"),
     ("bf16 store ties away from zero", "oracle/oracle.py", "np.round(np.ldexp(x, 8 - E))",
      "np.copysign(np.floor(np.abs(np.ldexp(x, 8 - E)) + 0.5), x)"),
+    ("Q head norm over the whole row", "oracle/oracle.py",
+     "    q = q / np.sqrt(np.mean(q * q, axis=-1, keepdims=True) + eps)\n",
+     "    q = q / np.sqrt(np.mean(q * q, axis=(-2, -1), keepdims=True) + eps)\n"),
+    ("Q second weight transposed", "oracle/oracle.py", "q = (qr @ _f64(wq_b).T).reshape(M, H, D)",
+     "q = (qr @ _f64(wq_b)).reshape(M, H, D)"),
+    ("Q heads dim-major", "oracle/oracle.py", "q = (qr @ _f64(wq_b).T).reshape(M, H, D)",
+     "q = (qr @ _f64(wq_b).T).reshape(M, D, H).transpose(0, 2, 1).copy()"),
+    ("Q gain dropped", "oracle/oracle.py", " + eps) * _f64(gamma_q)[None, :]", " + eps)"),
+    ("Q RoPE on the leading dims", "oracle/oracle.py", "q[m, h, D - rope_dim:] = rope(q[m, h, D - rope_dim:],",
+     "q[m, h, :rope_dim] = rope(q[m, h, :rope_dim],"),
+    ("Q row position ignores the token offset", "oracle/oracle.py", "return pos[m // S] + m % S",
+     "return pos[m // S] + 0 * m"),
+    ("O heads dealt to groups round-robin", "oracle/oracle.py", "og = O.reshape(M, groups, -1)",
+     "og = O.reshape(M, -1, groups, O.shape[-1]).transpose(0, 2, 1, 3).reshape(M, groups, -1)"),
+    ("O group weight transposed", "oracle/oracle.py", "r[:, g, :] = og[:, g, :] @ Wa[g].T",
+     "r[:, g, :] = (og[:, g, :] @ Wa[g].reshape(Wa.shape[2], Wa.shape[1]))"),
+    ("O store skipped", "oracle/oracle.py", "        r = _f64(round_bf16(r))\n", "        pass\n"),
+    ("Q store skipped", "oracle/oracle.py", "        qr = _f64(round_bf16(qr))\n", "        pass\n"),
 ]
+
+
 
 
 def _tree(dst):

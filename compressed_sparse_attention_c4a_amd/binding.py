@@ -54,6 +54,10 @@ def load() -> ctypes.CDLL:
         "hca_attn": ([vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i32, i32, i32, i32, i32, i32, i32, i32, i32, f32, f32,
                       i32, vp], i32),
         "swa_attn": ([vp, vp, vp, vp, vp, vp, vp, vp, sz, i32, i32, i32, i32, i32, i32, i32, f32, f32, i32, vp], i32),
+        "csa_q_proj_workspace_size": ([i32, i32, i32, i32, i32], sz),
+        "csa_q_proj": ([vp, vp, vp, vp, vp, vp, vp, vp, sz, i32, i32, i32, i32, i32, i32, i32, f32, f32, vp], i32),
+        "csa_o_proj_workspace_size": ([i32, i32, i32, i32, i32, i32], sz),
+        "csa_o_proj": ([vp, vp, vp, vp, vp, vp, sz, i32, i32, i32, i32, i32, i32, vp], i32),
     }
     for name, (args, res) in sigs.items():
         fn = getattr(L, name)
@@ -307,3 +311,47 @@ def swa_attn(q, win_kv, win_pos0, sink, q_pos, out, lse=None, *, rope_dim: int, 
             _ptr(lse, torch.float32, "lse"), _ptr(workspace, None, "workspace"), ws_bytes, B, S, H, D, rope_dim, W_cap,
             window, scale, rope_base, _dtype_code(q), _stream(stream))
     return _run("swa_attn", args, prepare, keep=(workspace,))
+
+
+def csa_q_proj_workspace_size(M: int, d_model: int, q_rank: int, H: int, D: int) -> int:
+    return load().csa_q_proj_workspace_size(M, d_model, q_rank, H, D)
+
+
+def csa_q_proj(x, wq_a, gamma_q, wq_b, pos, qr, q, *, B: int, S: int, rope_dim: int, eps: float = 1e-6,
+               rope_base: float = 10000.0, workspace=None, stream=None, prepare: bool = False):
+    """Low-rank query: x [B*S, d_model] -> qr [B*S, q_rank], q [B*S, H, D]
+    (bf16 throughout)."""
+    M, d_model = x.shape
+    q_rank = wq_a.shape[0]
+    H, D = q.shape[-2], q.shape[-1]
+    if M != B * S:
+        raise ValueError(f"x has {M} rows, expected B*S = {B * S}")
+    if workspace is None:
+        workspace = torch.empty(csa_q_proj_workspace_size(M, d_model, q_rank, H, D), dtype=torch.uint8,
+                                device=x.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    bf = torch.bfloat16
+    args = (_ptr(x, bf, "x"), _ptr(wq_a, bf, "wq_a"), _ptr(gamma_q, torch.float32, "gamma_q"), _ptr(wq_b, bf, "wq_b"),
+            _ptr(pos, torch.int32, "pos"), _ptr(qr, bf, "qr"), _ptr(q, bf, "q"), _ptr(workspace, None, "workspace"),
+            ws_bytes, B, S, d_model, q_rank, H, D, rope_dim, eps, rope_base, _stream(stream))
+    return _run("csa_q_proj", args, prepare, keep=(workspace,))
+
+
+def csa_o_proj_workspace_size(M: int, H: int, D: int, groups: int, o_rank: int, d_model: int) -> int:
+    return load().csa_o_proj_workspace_size(M, H, D, groups, o_rank, d_model)
+
+
+def csa_o_proj(o, wo_a, wo_b, r, y, *, groups: int, workspace=None, stream=None, prepare: bool = False):
+    """Grouped output projection: o [M, H, D] -> r [M, groups*o_rank] ->
+    y [M, d_model] (bf16 throughout)."""
+    M, H, D = o.shape
+    o_rank = wo_a.shape[1]
+    d_model = wo_b.shape[0]
+    if workspace is None:
+        workspace = torch.empty(csa_o_proj_workspace_size(M, H, D, groups, o_rank, d_model), dtype=torch.uint8,
+                                device=o.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    bf = torch.bfloat16
+    args = (_ptr(o, bf, "o"), _ptr(wo_a, bf, "wo_a"), _ptr(wo_b, bf, "wo_b"), _ptr(r, bf, "r"), _ptr(y, bf, "y"),
+            _ptr(workspace, None, "workspace"), ws_bytes, M, H, D, groups, o_rank, d_model, _stream(stream))
+    return _run("csa_o_proj", args, prepare, keep=(workspace,))

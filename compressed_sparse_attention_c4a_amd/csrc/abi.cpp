@@ -399,4 +399,104 @@ int swa_attn(const void* q, const void* win_kv, const int32_t* win_pos0, const f
                                             rope_base, dtype, (hipStream_t)stream));
 }
 
+// ---- projections around the attention --------------------------------------
+static size_t max_sz(size_t a, size_t b) { return a > b ? a : b; }
+
+size_t csa_q_proj_workspace_size(int M, int d_model, int q_rank, int H, int D) {
+  if (M < 1 || d_model < 512 || q_rank < 512 || H < 1 || D < 2) return 0;
+  return max_sz(csa_host::gemm_partial_bytes(1, M, q_rank, d_model),
+                csa_host::gemm_partial_bytes(1, M, H * D, q_rank));
+}
+
+int csa_q_proj(const void* x, const void* wq_a, const float* gamma_q, const void* wq_b, const int32_t* pos, void* qr,
+               void* q, void* workspace, size_t workspace_bytes, int B, int S, int d_model, int q_rank, int H, int D,
+               int rope_dim, float eps, float rope_base, csa_stream_t stream) {
+  const char* fn = "csa_q_proj";
+  REQ_PTR(x);
+  REQ_PTR(wq_a);
+  REQ_PTR(gamma_q);
+  REQ_PTR(wq_b);
+  REQ_PTR(pos);
+  REQ_PTR(qr);
+  REQ_PTR(q);
+  REQ(B >= 1 && S >= 1 && (long)B * S <= (1 << 20), "%s: B*S must be in [1, 2^20]", fn);
+  REQ(d_model >= 512 && d_model % 512 == 0, "%s: d_model must be a positive multiple of 512", fn);
+  REQ(q_rank >= 512 && q_rank % 512 == 0 && q_rank <= 2048, "%s: q_rank must be 512, 1024, 1536 or 2048", fn);
+  REQ(H >= 1 && D >= 256 && D <= 2048 && D % 256 == 0, "%s: D must be a multiple of 256 in [256, 2048]", fn);
+  REQ((long)H * D <= (1 << 20), "%s: H*D must be <= 2^20", fn);
+  REQ(rope_dim >= 0 && rope_dim <= D && rope_dim % 2 == 0, "%s: rope_dim must be even and <= D", fn);
+  REQ(eps >= 0.0f && std::isfinite(eps), "%s: eps must be finite and >= 0", fn);
+  const int M = B * S;
+  const size_t need = csa_q_proj_workspace_size(M, d_model, q_rank, H, D);
+  if (!workspace || workspace_bytes < need)
+    return fail(CSA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed (got %zu)", fn, need, workspace_bytes);
+  REQ_PTR(workspace);
+  hipStream_t st = (hipStream_t)stream;
+  float* part = (float*)workspace;
+  int ks = 0;
+  hipError_t e = csa_host::launch_gemm_nt(x, wq_a, part, 1, M, q_rank, d_model, d_model, d_model, 0, 0, &ks, st);
+  if (e == hipSuccess)
+    e = csa_host::launch_rows_finish(part, qr, gamma_q, nullptr, M, q_rank, q_rank, q_rank, ks, 1, 0, 1, eps,
+                                     rope_base, st);
+  if (e == hipSuccess)
+    e = csa_host::launch_gemm_nt(qr, wq_b, part, 1, M, H * D, q_rank, q_rank, q_rank, 0, 0, &ks, st);
+  if (e == hipSuccess)
+    e = csa_host::launch_rows_finish(part, q, nullptr, pos, M, H * D, H * D, D, ks, 1, rope_dim, S, eps, rope_base,
+                                     st);
+  return launched(fn, e);
+}
+
+// Segment width of a plain (no norm) finishing pass: 1024 or 512 or 256
+// columns, whichever divides the row.
+static int finish_seg(int ncols) {
+  for (int s = 1024; s >= 256; s >>= 1)
+    if (ncols % s == 0) return s;
+  return 0;
+}
+
+size_t csa_o_proj_workspace_size(int M, int H, int D, int groups, int o_rank, int d_model) {
+  if (M < 1 || H < 1 || D < 1 || groups < 1 || H % groups != 0 || o_rank < 1 || d_model < 1) return 0;
+  const int gdim = H / groups * D;
+  return max_sz(csa_host::gemm_partial_bytes(groups, M, o_rank, gdim),
+                csa_host::gemm_partial_bytes(1, M, d_model, groups * o_rank));
+}
+
+int csa_o_proj(const void* o, const void* wo_a, const void* wo_b, void* r, void* y, void* workspace,
+               size_t workspace_bytes, int M, int H, int D, int groups, int o_rank, int d_model,
+               csa_stream_t stream) {
+  const char* fn = "csa_o_proj";
+  REQ_PTR(o);
+  REQ_PTR(wo_a);
+  REQ_PTR(wo_b);
+  REQ_PTR(r);
+  REQ_PTR(y);
+  REQ(M >= 1 && M <= (1 << 20), "%s: M must be in [1, 2^20]", fn);
+  REQ(H >= 1 && D >= 1 && groups >= 1 && H % groups == 0, "%s: groups must divide H", fn);
+  const long gdim = (long)H / groups * D;
+  REQ(gdim % 512 == 0 && (long)H * D <= (1 << 20), "%s: (H/groups)*D must be a multiple of 512 (H*D <= 2^20)", fn);
+  REQ(o_rank >= 64 && o_rank % 64 == 0, "%s: o_rank must be a positive multiple of 64", fn);
+  REQ((long)groups * o_rank % 512 == 0 && (long)groups * o_rank <= (1 << 20),
+      "%s: groups*o_rank must be a multiple of 512 (<= 2^20)", fn);
+  REQ(d_model >= 256 && d_model % 256 == 0 && d_model <= (1 << 20), "%s: d_model must be a multiple of 256", fn);
+  const size_t need = csa_o_proj_workspace_size(M, H, D, groups, o_rank, d_model);
+  if (!workspace || workspace_bytes < need)
+    return fail(CSA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed (got %zu)", fn, need, workspace_bytes);
+  REQ_PTR(workspace);
+  hipStream_t st = (hipStream_t)stream;
+  float* part = (float*)workspace;
+  const int rcols = groups * o_rank;
+  int ks = 0;
+  hipError_t e = csa_host::launch_gemm_nt(o, wo_a, part, groups, M, o_rank, (int)gdim, H * D, (int)gdim, gdim,
+                                          (long)o_rank * gdim, &ks, st);
+  if (e == hipSuccess)
+    e = csa_host::launch_rows_finish(part, r, nullptr, nullptr, M, rcols, o_rank, finish_seg(rcols), ks, 0, 0, 1,
+                                     0.f, 10000.f, st);
+  if (e == hipSuccess)
+    e = csa_host::launch_gemm_nt(r, wo_b, part, 1, M, d_model, rcols, rcols, rcols, 0, 0, &ks, st);
+  if (e == hipSuccess)
+    e = csa_host::launch_rows_finish(part, y, nullptr, nullptr, M, d_model, d_model, finish_seg(d_model), ks, 0, 0,
+                                     1, 0.f, 10000.f, st);
+  return launched(fn, e);
+}
+
 }  // extern "C"

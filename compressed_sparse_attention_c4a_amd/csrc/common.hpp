@@ -237,4 +237,10 @@ hipError_t launch_attn(const void* q, const void* cmp, const int32_t* topk_idx, 
                        const int32_t* win_pos0, const float* sink, const int32_t* q_pos, void* out, float* lse,
                        void* ws, int B, int S, int H, int D, int rope_dim, int N_cap, int W_cap, int window,
                        float scale, float base, int dtype, hipStream_t st);
+size_t gemm_partial_bytes(int groups, int M, int N, int K);
+hipError_t launch_gemm_nt(const void* A, const void* Bw, float* C, int groups, int M, int N, int K, int lda, int ldb,
+                          long sa, long sb, int* ksplit_out, hipStream_t st);
+hipError_t launch_rows_finish(const float* part, void* out, const float* gamma, const int32_t* pos, int M, int ncols,
+                              int gcols, int seg, int ksplit, int norm, int rope_dim, int S, float eps, float base,
+                              hipStream_t st);
 }  // namespace csa_host

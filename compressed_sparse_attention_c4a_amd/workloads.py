@@ -52,12 +52,16 @@ class Draw:
             out += np.float32(shift)
         return out.reshape(shape)
 
-    def bf16(self, shape) -> np.ndarray:
+    def bf16(self, shape, scale: float = 1.0) -> np.ndarray:
+        """N(0, scale^2) draws in float32, rounded to bf16 bit patterns."""
         n = int(np.prod(shape))
         out = np.empty(n, dtype=np.uint16)
         for i in range(0, n, CHUNK):
             m = min(CHUNK, n - i)
-            out[i:i + m] = bf16_bits(self.rng.standard_normal(m, dtype=np.float32))
+            v = self.rng.standard_normal(m, dtype=np.float32)
+            if scale != 1.0:
+                v *= np.float32(scale)
+            out[i:i + m] = bf16_bits(v)
         return out.reshape(shape)
 
     def data(self, shape, dtype: str) -> np.ndarray:
@@ -238,4 +242,50 @@ def slice_batch(inp: dict, n: int) -> dict:
         if key == "shape":
             continue
         out[key] = val if (val is None or key in per_head) else val[:n]
+    return out
+
+
+@dataclasses.dataclass
+class ProjShape:
+    """Sizes of the projections around one attention layer ("DeepSeek-V4-Pro
+    架构": d_model 7168, low-rank Q of rank 1536 into 128 heads x 512, output
+    in 16 groups of 8 heads, each projected to 1024, then 16384 -> 7168)."""
+    name: str
+    B: int = 32
+    S: int = 1
+    q_pos: int = 32767
+    d_model: int = 7168
+    q_rank: int = 1536
+    H: int = 128
+    D: int = 512
+    rope: int = 64
+    groups: int = 16
+    o_rank: int = 1024
+    seed: int = 7
+
+    @property
+    def M(self) -> int:
+        return self.B * self.S
+
+
+def proj_decode_32k(B: int = 32) -> ProjShape:
+    """Decode projections: B tokens at position 32767."""
+    return ProjShape(name="proj_decode_32k", B=B)
+
+
+def generate_proj(ps: ProjShape, seed: Optional[int] = None) -> dict:
+    """Inputs and random-init weights of the projections, in a fixed order.
+    Activations are N(0,1); every weight matrix is N(0, 1/K) for its input
+    width K, so products stay O(1); gamma_q is 1 + 0.1 N(0,1)."""
+    dr = Draw(ps.seed if seed is None else seed)
+    gdim = ps.H // ps.groups * ps.D
+    out = {"shape": ps}
+    out["x"] = dr.bf16((ps.M, ps.d_model))
+    out["wq_a"] = dr.bf16((ps.q_rank, ps.d_model), scale=1.0 / math.sqrt(ps.d_model))
+    out["gamma_q"] = dr.f32((ps.q_rank,), scale=0.1, shift=1.0)
+    out["wq_b"] = dr.bf16((ps.H * ps.D, ps.q_rank), scale=1.0 / math.sqrt(ps.q_rank))
+    out["o"] = dr.bf16((ps.M, ps.H, ps.D))
+    out["wo_a"] = dr.bf16((ps.groups, ps.o_rank, gdim), scale=1.0 / math.sqrt(gdim))
+    out["wo_b"] = dr.bf16((ps.d_model, ps.groups * ps.o_rank), scale=1.0 / math.sqrt(ps.groups * ps.o_rank))
+    out["pos"] = np.full((ps.B,), ps.q_pos, dtype=np.int32)
     return out

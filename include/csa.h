@@ -251,6 +251,51 @@ int swa_attn(const void* q, const void* win_kv, const int32_t* win_pos0, const f
              void* out, float* lse, void* workspace, size_t workspace_bytes, int B, int S, int H, int D, int rope_dim,
              int W_cap, int window, float softmax_scale, float rope_base, int dtype, csa_stream_t stream);
 
+/*
+ * csa_q_proj -- low-rank query projection, [P1] "低秩 Q：两次矩阵乘法接起来":
+ *   qr = RMSNorm(x wq_a^T) with gain gamma_q;  q = qr wq_b^T as [M, H, D];
+ *   each head divided by sqrt(mean over D of q^2 + eps); RoPE (the pair
+ *   rotation of the compressed entries) on the last rope_dim dims of every
+ *   head at the row's position.  Rows are M = B*S tokens, sequence-major:
+ *   row m is token m % S of sequence m / S, at position pos[m / S] + m % S.
+ *
+ * x: [M, d_model] bf16; wq_a: [q_rank, d_model] bf16; gamma_q: [q_rank]
+ *   fp32; wq_b: [H*D, q_rank] bf16; pos: [B] device int32.
+ * qr: [M, q_rank] bf16, written (it is also the second product's input);
+ * q: [M, H, D] bf16, written: the attention's query layout.
+ * Products accumulate in fp32; qr and q are rounded to bf16 once.
+ * workspace: csa_q_proj_workspace_size(M, ...) bytes, device memory of fp32
+ *   split-K partials; no initialisation needed; calls that may overlap need
+ *   separate workspaces.  The call enqueues four kernels on `stream`.
+ * Requires: d_model a multiple of 512; q_rank in {512, 1024, 1536, 2048};
+ *   D a multiple of 256 in [256, 2048]; rope_dim even <= D; eps >= 0.
+ */
+size_t csa_q_proj_workspace_size(int M, int d_model, int q_rank, int H, int D);
+int csa_q_proj(const void* x, const void* wq_a, const float* gamma_q, const void* wq_b, const int32_t* pos, void* qr,
+               void* q, void* workspace, size_t workspace_bytes, int B, int S, int d_model, int q_rank, int H, int D,
+               int rope_dim, float eps, float rope_base, csa_stream_t stream);
+
+/*
+ * csa_o_proj -- grouped output projection, [P1] "输出投影也分组，并且降低中间维度"
+ * (the inverse RoPE that section starts with is already in the attention
+ * output): heads h = g*(H/groups) .. (g+1)*(H/groups)-1 form group g;
+ *   r[m, g] = o[m, group g's (H/groups)*D dims] wo_a[g]^T;
+ *   y = r (flattened group-major) wo_b^T.
+ *
+ * o: [M, H, D] bf16 (attention output); wo_a: [groups, o_rank, H/groups*D]
+ *   bf16; wo_b: [d_model, groups*o_rank] bf16.
+ * r: [M, groups*o_rank] bf16, written; y: [M, d_model] bf16, written.
+ * Products accumulate in fp32; r and y are rounded to bf16 once.
+ * workspace: csa_o_proj_workspace_size(M, ...) bytes of fp32 partials, as
+ *   for csa_q_proj.  The call enqueues four kernels on `stream`.
+ * Requires: groups divides H; (H/groups)*D and groups*o_rank multiples of
+ *   512; o_rank a multiple of 64; d_model a multiple of 256.
+ */
+size_t csa_o_proj_workspace_size(int M, int H, int D, int groups, int o_rank, int d_model);
+int csa_o_proj(const void* o, const void* wo_a, const void* wo_b, void* r, void* y, void* workspace,
+               size_t workspace_bytes, int M, int H, int D, int groups, int o_rank, int d_model,
+               csa_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

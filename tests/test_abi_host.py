@@ -124,3 +124,36 @@ def test_binding_refuses_host_tensors():
     x = torch.zeros(4)
     with pytest.raises(ValueError):
         K._ptr(x, None, "x")
+
+
+def test_q_proj_validation(lib):
+    """Argument checks of csa_q_proj, all rejected before any launch."""
+    def qp(x=P, wa=P, g=P, wb=P, pos=P, qr=P, q=P, B=32, S=1, dm=7168, qrk=1536, H=128, D=512, rope=64, ws=P,
+           nws=1 << 30):
+        return lib.csa_q_proj(x, wa, g, wb, pos, qr, q, ws, nws, B, S, dm, qrk, H, D, rope, 1e-6, 10000.0, None)
+    assert qp(wb=None) == CSA_ERR_NULL
+    assert qp(qr=MIS) == CSA_ERR_ALIGN
+    assert qp(qrk=700) == CSA_ERR_SHAPE
+    assert qp(qrk=4096) == CSA_ERR_SHAPE
+    assert qp(dm=7000) == CSA_ERR_SHAPE
+    assert qp(D=500) == CSA_ERR_SHAPE
+    assert qp(rope=65) == CSA_ERR_SHAPE
+    assert qp(B=0) == CSA_ERR_SHAPE
+    need = lib.csa_q_proj_workspace_size(32, 7168, 1536, 128, 512)
+    assert need >= 32 * 128 * 512 * 4
+    assert qp(ws=None) == CSA_ERR_WORKSPACE
+    assert qp(nws=need - 1) == CSA_ERR_WORKSPACE
+
+
+def test_o_proj_validation(lib):
+    def op(o=P, wa=P, wb=P, r=P, y=P, M=32, H=128, D=512, G=16, orank=1024, dm=7168, ws=P, nws=1 << 30):
+        return lib.csa_o_proj(o, wa, wb, r, y, ws, nws, M, H, D, G, orank, dm, None)
+    assert op(y=None) == CSA_ERR_NULL
+    assert op(wa=MIS) == CSA_ERR_ALIGN
+    assert op(G=3) == CSA_ERR_SHAPE          # does not divide H
+    assert op(orank=1000) == CSA_ERR_SHAPE
+    assert op(dm=7100) == CSA_ERR_SHAPE
+    assert op(M=0) == CSA_ERR_SHAPE
+    need = lib.csa_o_proj_workspace_size(32, 128, 512, 16, 1024, 7168)
+    assert need >= 16 * 32 * 1024 * 4
+    assert op(nws=need - 1) == CSA_ERR_WORKSPACE

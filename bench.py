@@ -163,6 +163,55 @@ def copy_calibration(nbytes: int, reps: int = 5):
     print(json.dumps({"copy_calibration_bytes": nbytes, "launches": reps}))
 
 
+def measure_projections(B: int, iters: int = 30):
+    """Time the projections around one attention layer at decode (B tokens):
+    csa_q_proj (x -> qr -> q, with the norms and RoPE) and csa_o_proj
+    (o -> r -> y), weights packed once beforehand.  The 592 MB of bf16
+    weights exceed the 256 MB Infinity Cache, so every call streams them from
+    HBM; algorithmic bytes = weights + activations read and written once."""
+    import torch
+    from compressed_sparse_attention_c4a_amd import binding as K
+    from compressed_sparse_attention_c4a_amd import path as P
+    from compressed_sparse_attention_c4a_amd import workloads as W
+
+    ps = W.proj_decode_32k(B)
+    dev = P.to_device(W.generate_proj(ps), "cuda")
+    for k in ("wq_a", "wq_b", "wo_a", "wo_b"):
+        dev[k] = K.csa_pack_weights(dev[k])
+    M, bf = ps.M, torch.bfloat16
+    qr = torch.empty(M, ps.q_rank, dtype=bf, device="cuda")
+    q = torch.empty(M, ps.H, ps.D, dtype=bf, device="cuda")
+    r = torch.empty(M, ps.groups * ps.o_rank, dtype=bf, device="cuda")
+    y = torch.empty(M, ps.d_model, dtype=bf, device="cuda")
+    stream = torch.cuda.current_stream()
+    cq = K.csa_q_proj(dev["x"], dev["wq_a"], dev["gamma_q"], dev["wq_b"], dev["pos"], qr, q, B=ps.B, S=ps.S,
+                      rope_dim=ps.rope, stream=stream, prepare=True)
+    co = K.csa_o_proj(dev["o"], dev["wo_a"], dev["wo_b"], r, y, groups=ps.groups, stream=stream, prepare=True)
+    HD = ps.H * ps.D
+    w_q = 2 * (ps.q_rank * ps.d_model + HD * ps.q_rank)
+    w_o = 2 * (ps.o_rank * HD + ps.d_model * ps.groups * ps.o_rank)
+    alg_q = w_q + 2 * M * (ps.d_model + 2 * ps.q_rank + HD) + 4 * ps.q_rank
+    alg_o = w_o + 2 * M * (HD + 2 * ps.groups * ps.o_rank + ps.d_model)
+    fl_q = 2 * M * (ps.d_model * ps.q_rank + ps.q_rank * HD)
+    fl_o = 2 * M * (HD * ps.o_rank + ps.groups * ps.o_rank * ps.d_model)
+    out = {"workload": ps.name, "tokens": M, "d_model": ps.d_model, "q_rank": ps.q_rank,
+           "groups": ps.groups, "o_rank": ps.o_rank, "weight_bytes": w_q + w_o}
+    for name, c, alg, fl in [("q_proj", cq, alg_q, fl_q), ("o_proj", co, alg_o, fl_o)]:
+        for _ in range(5):
+            c()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(iters):
+            c()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        sec = e0.elapsed_time(e1) * 1e-3 / iters
+        out[name] = {"us": round(sec * 1e6, 2), **roofline_of(alg, fl, sec)}
+    out["us_per_layer"] = round(out["q_proj"]["us"] + out["o_proj"]["us"], 2)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -172,6 +221,7 @@ def main():
     ap.add_argument("--rotate", type=int, default=0, help="input copies to rotate (0: enough to defeat the MALL)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="wall time of the CPU oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-projections", action="store_true", help="skip the Q/O projection measurement")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes (HBM counter calibration) and exit")
     args = ap.parse_args()
@@ -270,6 +320,8 @@ def main():
              "per_call": {c: roofline_of(per[c]["bytes"] * Q, per[c]["flops"] * Q, avg_probe[c] * 1e-3)
                           for c in calls}}
 
+    proj = measure_projections(sh.B) if (sh.S == 1 and not args.no_projections) else None
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(inp, args.cpu_seconds)
@@ -286,6 +338,9 @@ def main():
         "roofline": roof,
         "whole_step": whole,
         "call_us": {c: round(v * 1e3, 2) for c, v in avg_probe.items()},
+        # the projections around the same layer (not part of `value`): the
+        # decode step of a whole attention block adds their time
+        "projections": proj,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res))

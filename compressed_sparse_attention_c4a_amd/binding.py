@@ -54,6 +54,7 @@ def load() -> ctypes.CDLL:
         "hca_attn": ([vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i32, i32, i32, i32, i32, i32, i32, i32, i32, f32, f32,
                       i32, vp], i32),
         "swa_attn": ([vp, vp, vp, vp, vp, vp, vp, vp, sz, i32, i32, i32, i32, i32, i32, i32, f32, f32, i32, vp], i32),
+        "csa_pack_weights": ([vp, vp, i32, i32, i32, vp], i32),
         "csa_q_proj_workspace_size": ([i32, i32, i32, i32, i32], sz),
         "csa_q_proj": ([vp, vp, vp, vp, vp, vp, vp, vp, sz, i32, i32, i32, i32, i32, i32, i32, f32, f32, vp], i32),
         "csa_o_proj_workspace_size": ([i32, i32, i32, i32, i32, i32], sz),
@@ -313,6 +314,19 @@ def swa_attn(q, win_kv, win_pos0, sink, q_pos, out, lse=None, *, rope_dim: int, 
     return _run("swa_attn", args, prepare, keep=(workspace,))
 
 
+def csa_pack_weights(w, packed=None, *, stream=None, prepare: bool = False):
+    """Pack a bf16 weight [N, K] (or a group stack [G, N, K]) into the layout
+    csa_q_proj / csa_o_proj read.  Returns the packed tensor (same shape and
+    size; the contents are a permutation)."""
+    groups = 1 if w.dim() == 2 else w.shape[0]
+    N, Kd = w.shape[-2], w.shape[-1]
+    if packed is None:
+        packed = torch.empty_like(w)
+    args = (_ptr(w, torch.bfloat16, "w"), _ptr(packed, torch.bfloat16, "packed"), groups, N, Kd, _stream(stream))
+    _run("csa_pack_weights", args, prepare)
+    return packed
+
+
 def csa_q_proj_workspace_size(M: int, d_model: int, q_rank: int, H: int, D: int) -> int:
     return load().csa_q_proj_workspace_size(M, d_model, q_rank, H, D)
 
@@ -320,7 +334,7 @@ def csa_q_proj_workspace_size(M: int, d_model: int, q_rank: int, H: int, D: int)
 def csa_q_proj(x, wq_a, gamma_q, wq_b, pos, qr, q, *, B: int, S: int, rope_dim: int, eps: float = 1e-6,
                rope_base: float = 10000.0, workspace=None, stream=None, prepare: bool = False):
     """Low-rank query: x [B*S, d_model] -> qr [B*S, q_rank], q [B*S, H, D]
-    (bf16 throughout)."""
+    (bf16 throughout); wq_a and wq_b packed by csa_pack_weights."""
     M, d_model = x.shape
     q_rank = wq_a.shape[0]
     H, D = q.shape[-2], q.shape[-1]
@@ -343,7 +357,8 @@ def csa_o_proj_workspace_size(M: int, H: int, D: int, groups: int, o_rank: int, 
 
 def csa_o_proj(o, wo_a, wo_b, r, y, *, groups: int, workspace=None, stream=None, prepare: bool = False):
     """Grouped output projection: o [M, H, D] -> r [M, groups*o_rank] ->
-    y [M, d_model] (bf16 throughout)."""
+    y [M, d_model] (bf16 throughout); wo_a and wo_b packed by
+    csa_pack_weights."""
     M, H, D = o.shape
     o_rank = wo_a.shape[1]
     d_model = wo_b.shape[0]

@@ -402,6 +402,19 @@ int swa_attn(const void* q, const void* win_kv, const int32_t* win_pos0, const f
 // ---- projections around the attention --------------------------------------
 static size_t max_sz(size_t a, size_t b) { return a > b ? a : b; }
 
+int csa_pack_weights(const void* w, void* packed, int groups, int N, int K, csa_stream_t stream) {
+  const char* fn = "csa_pack_weights";
+  REQ_PTR(w);
+  REQ_PTR(packed);
+  REQ(groups >= 1 && N >= 64 && N % 64 == 0 && K >= 512 && K % 512 == 0,
+      "%s: N must be a positive multiple of 64 and K of 512", fn);
+  REQ((double)groups * N * (double)K <= 1e12, "%s: groups*N*K too large", fn);
+  const size_t bytes = (size_t)groups * N * (size_t)K * 2;
+  const char *a = (const char*)w, *b = (const char*)packed;
+  REQ(a + bytes <= b || b + bytes <= a, "%s: w and packed overlap", fn);
+  return launched(fn, csa_host::launch_pack_weights(w, packed, groups, N, K, (hipStream_t)stream));
+}
+
 size_t csa_q_proj_workspace_size(int M, int d_model, int q_rank, int H, int D) {
   if (M < 1 || d_model < 512 || q_rank < 512 || H < 1 || D < 2) return 0;
   return max_sz(csa_host::gemm_partial_bytes(1, M, q_rank, d_model),
@@ -434,12 +447,12 @@ int csa_q_proj(const void* x, const void* wq_a, const float* gamma_q, const void
   hipStream_t st = (hipStream_t)stream;
   float* part = (float*)workspace;
   int ks = 0;
-  hipError_t e = csa_host::launch_gemm_nt(x, wq_a, part, 1, M, q_rank, d_model, d_model, d_model, 0, 0, &ks, st);
+  hipError_t e = csa_host::launch_gemm_nt(x, wq_a, part, 1, M, q_rank, d_model, d_model, 0, 0, &ks, st);
   if (e == hipSuccess)
     e = csa_host::launch_rows_finish(part, qr, gamma_q, nullptr, M, q_rank, q_rank, q_rank, ks, 1, 0, 1, eps,
                                      rope_base, st);
   if (e == hipSuccess)
-    e = csa_host::launch_gemm_nt(qr, wq_b, part, 1, M, H * D, q_rank, q_rank, q_rank, 0, 0, &ks, st);
+    e = csa_host::launch_gemm_nt(qr, wq_b, part, 1, M, H * D, q_rank, q_rank, 0, 0, &ks, st);
   if (e == hipSuccess)
     e = csa_host::launch_rows_finish(part, q, nullptr, pos, M, H * D, H * D, D, ks, 1, rope_dim, S, eps, rope_base,
                                      st);
@@ -486,13 +499,13 @@ int csa_o_proj(const void* o, const void* wo_a, const void* wo_b, void* r, void*
   float* part = (float*)workspace;
   const int rcols = groups * o_rank;
   int ks = 0;
-  hipError_t e = csa_host::launch_gemm_nt(o, wo_a, part, groups, M, o_rank, (int)gdim, H * D, (int)gdim, gdim,
+  hipError_t e = csa_host::launch_gemm_nt(o, wo_a, part, groups, M, o_rank, (int)gdim, H * D, gdim,
                                           (long)o_rank * gdim, &ks, st);
   if (e == hipSuccess)
     e = csa_host::launch_rows_finish(part, r, nullptr, nullptr, M, rcols, o_rank, finish_seg(rcols), ks, 0, 0, 1,
                                      0.f, 10000.f, st);
   if (e == hipSuccess)
-    e = csa_host::launch_gemm_nt(r, wo_b, part, 1, M, d_model, rcols, rcols, rcols, 0, 0, &ks, st);
+    e = csa_host::launch_gemm_nt(r, wo_b, part, 1, M, d_model, rcols, rcols, 0, 0, &ks, st);
   if (e == hipSuccess)
     e = csa_host::launch_rows_finish(part, y, nullptr, nullptr, M, d_model, d_model, finish_seg(d_model), ks, 0, 0,
                                      1, 0.f, 10000.f, st);

@@ -238,8 +238,9 @@ hipError_t launch_attn(const void* q, const void* cmp, const int32_t* topk_idx, 
                        void* ws, int B, int S, int H, int D, int rope_dim, int N_cap, int W_cap, int window,
                        float scale, float base, int dtype, hipStream_t st);
 size_t gemm_partial_bytes(int groups, int M, int N, int K);
-hipError_t launch_gemm_nt(const void* A, const void* Bw, float* C, int groups, int M, int N, int K, int lda, int ldb,
-                          long sa, long sb, int* ksplit_out, hipStream_t st);
+hipError_t launch_gemm_nt(const void* A, const void* Bp, float* C, int groups, int M, int N, int K, int lda, long sa,
+                          long sb, int* ksplit_out, hipStream_t st);
+hipError_t launch_pack_weights(const void* W, void* P, int groups, int N, int K, hipStream_t st);
 hipError_t launch_rows_finish(const float* part, void* out, const float* gamma, const int32_t* pos, int M, int ncols,
                               int gcols, int seg, int ksplit, int norm, int rope_dim, int S, float eps, float base,
                               hipStream_t st);

@@ -12,22 +12,30 @@
 //   y = r (flattened, group-major) Wo_b^T   Wo_b [d_model, groups*o_rank]
 // M = B*S rows.  Operands bf16, accumulation fp32, qr / q / r / y stored bf16.
 //
+// Weights are used in a packed layout (csa_pack_weights): a matrix W [N][K]
+// becomes blocks of 16 columns x 512 dims, block (c, h) at element offset
+// (c * K/512 + h) * 8192, holding for k-step j (32 dims) and lane (g, n) the
+// eight values W[16c + n][512h + 32j + 8g .. +8] at (j * 64 + 16g + n) * 8:
+// exactly the MFMA B-operand order of v_mfma_f32_16x16x32_bf16.  A wave that
+// owns 16 columns and a K split then reads one contiguous run, 1 KiB per
+// load instruction.  (HBM3E on this part streams fastest as a few long
+// contiguous runs per CU; rows read 64 bytes at a time across 16 rows of a
+// row-major weight run measurably slower.)
+//
 // gemm_nt_kernel computes split-K partials C[g][ks][m][n] = sum over k in
-// split ks of A_g[m][k] B_g[n][k] (both operands K-contiguous, the layout of
-// the activations and of the weights).  At decode M is a few dozen rows and
-// every weight is read once, so the kernel is an HBM stream of the weights:
-//   * a workgroup owns rows [m0, m0+TM) and one K split; it copies that A
-//     slab (TM x KC bf16) into LDS once, with direct global->LDS copies;
-//   * it then walks column tiles blockIdx.x, blockIdx.x + gridDim.x, ... ;
-//     each of its 4 waves owns 16 weight rows of the 64-column tile and
-//     streams them from HBM straight into MFMA B fragments
-//     (v_mfma_f32_16x16x32_bf16), PF k-steps of loads in flight; the ring of
-//     loads runs on across tile boundaries, so the stream never drains
-//     between tiles;
-//   * two consecutive k-steps of a lane group read one 128-byte line of a
-//     weight row.
-// Split-K partials are fp32 and summed in split order by rows_finish_kernel,
-// so results do not depend on scheduling.
+// split ks of A_g[m][k] W_g[n][k].  At decode M is a few dozen rows and every
+// weight is read once, so the kernel is an HBM stream of the weights:
+//   * about one workgroup per CU; a workgroup owns rows [m0, m0+TM), one K
+//     split of KC dims and a contiguous range of 64-column tiles;
+//   * it copies its A slab (TM x KC bf16, up to 128 KiB) into LDS once, with
+//     direct global->LDS copies, and reuses it for all of its tiles;
+//   * each of its 4 waves streams the packed run of its 16 columns into MFMA
+//     B fragments, PF k-steps of loads in flight, the ring running on across
+//     tile boundaries so the stream never drains between tiles.
+// The host picks KC and the tiles per workgroup from a small cost model
+// (busiest CU's weight bytes + partial traffic + A slab copies).  Split-K
+// partials are fp32 and summed in split order by rows_finish_kernel, so
+// results do not depend on scheduling.
 //
 // rows_finish_kernel: per output row and segment of `seg` columns, the sum of
 // the splits, then optionally an RMS normalisation over the segment (times a
@@ -44,11 +52,10 @@ namespace csa {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int PJ_TN = 64;  // columns per tile (16 per wave)
-#ifndef PJ_PF_SET
-#define PJ_PF_SET 16
-#endif
-constexpr int PJ_PF = PJ_PF_SET;  // k-steps (32 dims each) of weight loads in flight per wave
+constexpr int PJ_NW = 4;           // waves per workgroup
+constexpr int PJ_TN = 16 * PJ_NW;  // columns per tile (16 per wave)
+constexpr int PJ_CUS = 256;        // workgroups the plan aims for (one per CU)
+constexpr int PJ_PF = 16;  // k-steps (32 dims each) of weight loads in flight per wave
 // Every split holds whole 512-dim chunks (16 k-steps); the loop runs in
 // blocks of PJ_PF steps and its loads run PJ_PF steps ahead, so PJ_PF must
 // divide 16 or the last block would read past the split (and, in the last
@@ -57,11 +64,11 @@ static_assert(PJ_PF >= 1 && 16 % PJ_PF == 0, "PJ_PF must divide the 16 k-steps o
 
 struct GemmArgs {
   const bf16* A;   // [groups] x [M][lda]
-  const bf16* Bw;  // [groups] x [N][ldb]
+  const bf16* Bp;  // [groups] x packed W [N][K]
   float* C;        // [groups][ksplit][M][N]
-  int M, N, K, lda, ldb;
-  long sa, sb;     // group strides (elements) of A and B
-  int kc, ksplit, ntiles;
+  int M, N, K, lda;
+  long sa, sb;     // group strides (elements) of A and of the packed weights
+  int kc, ksplit, ntiles, tpw, gx, mtiles, groups;
 };
 
 // LDS bytes per A row: 16 bytes of padding puts rows n and n+1 four banks
@@ -69,21 +76,27 @@ struct GemmArgs {
 __host__ __device__ constexpr int pj_row_bytes(int kc) { return 2 * kc + 16; }
 
 template <int TM>
-__global__ __launch_bounds__(256) void gemm_nt_kernel(GemmArgs g) {
+__global__ __launch_bounds__(64 * PJ_NW) void gemm_nt_kernel(GemmArgs g) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds_a[];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63, gq = lane >> 4, n = lane & 15;
-  const int ks = blockIdx.y % g.ksplit, mt = blockIdx.y / g.ksplit, grp = blockIdx.z;
+  // 1-D grid, remapped so that the workgroups sharing an A slab (same split,
+  // row tile and group; consecutive bx) run on one XCD and share its L2
+  const int rows = g.ksplit * g.mtiles;
+  const int L = xcd_remap((int)blockIdx.x, g.gx * rows * g.groups);
+  const int bx = L % g.gx, by = (L / g.gx) % rows, grp = L / (g.gx * rows);
+  const int ks = by % g.ksplit, mt = by / g.ksplit;
   const int m0 = mt * TM, k0 = ks * g.kc;
-  const int kn = min(g.kc, g.K - k0);  // a multiple of 32 * PJ_PF (checked by the host)
-  const int nstep = kn >> 5;
+  const int kn = min(g.kc, g.K - k0);  // a multiple of 512 (K and kc are)
+  const int nstep = kn >> 5;           // a multiple of 16, so of PJ_PF
   const int AS = pj_row_bytes(g.kc);
   const bf16* A = g.A + grp * g.sa;
-  const bf16* Bw = g.Bw + grp * g.sb;
+  const bf16* Bp = g.Bp + grp * g.sb;
+  const int t0 = bx * g.tpw, t1 = min(t0 + g.tpw, g.ntiles);
 
   // A slab -> LDS, 1 KiB (512 dims) per copy; rows past M are zero
   const int chunks = kn >> 9;
-  for (int idx = wave; idx < TM * chunks; idx += 4) {
+  for (int idx = wave; idx < TM * chunks; idx += PJ_NW) {
     const int r = idx / chunks, c = idx - r * chunks;
     uint8_t* dst = lds_a + r * AS + 1024 * c;
     if (m0 + r < g.M)
@@ -92,29 +105,29 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmArgs g) {
       *(uint4*)(dst + 16 * lane) = make_uint4(0u, 0u, 0u, 0u);
   }
 
-  // weight row of this lane in tile t (columns past N read row N-1, never stored)
-  auto row_ptr = [&](int t) -> const bf16* {
-    const int col = min(t * PJ_TN + 16 * wave + n, g.N - 1);
-    return Bw + (size_t)col * g.ldb + k0 + 8 * gq;
+  // the packed run of this wave's 16 columns of tile t over this split:
+  // nstep KiB, k-step j at +512 j elements
+  const int kch = g.K >> 9;
+  auto run_ptr = [&](int t) -> const bf16* {
+    return Bp + ((size_t)(4 * t + wave) * kch + (k0 >> 9)) * 8192 + 8 * lane;
   };
-  int t = blockIdx.x;
-  const bf16* cur = row_ptr(t);
+  const bf16* cur = run_ptr(t0);
   bf16x8_t bfrag[PJ_PF];
 #pragma unroll
-  for (int j = 0; j < PJ_PF; ++j) bfrag[j] = *(const bf16x8_t*)(cur + 32 * j);
+  for (int j = 0; j < PJ_PF; ++j) bfrag[j] = *(const bf16x8_t*)(cur + 512 * j);
   WAIT_VMCNT(PJ_PF);  // this wave's A copies (issued first) are in LDS
   lds_barrier();      // ... and every wave's; the weight loads stay in flight
 
-  for (; t < g.ntiles; t += gridDim.x) {
-    const int tn = t + gridDim.x;
-    const bf16* nxt = row_ptr(tn < g.ntiles ? tn : t);
+  for (int t = t0; t < t1; ++t) {
+    // the last tile's ring re-reads its own run's start (in bounds, unused)
+    const bf16* nxt = run_ptr(t + 1 < t1 ? t + 1 : t);
     f32x4_t acc[TM / 16];
 #pragma unroll
     for (int mb = 0; mb < TM / 16; ++mb) acc[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     for (int j0 = 0; j0 < nstep; j0 += PJ_PF) {
-      // the loads issued in this block are PF steps ahead: the rest of this
-      // tile's row, or the start of the next tile's row in the last block
-      const bf16* lb = (j0 + PJ_PF < nstep) ? cur + 32 * (j0 + PJ_PF) : nxt;
+      // the loads issued in this block are PF steps ahead: further along this
+      // run, or the start of the next tile's run in the last block
+      const bf16* lb = (j0 + PJ_PF < nstep) ? cur + 512 * (j0 + PJ_PF) : nxt;
 #pragma unroll
       for (int j = 0; j < PJ_PF; ++j) {
         const uint8_t* ap = lds_a + n * AS + 2 * (32 * (j0 + j) + 8 * gq);
@@ -125,31 +138,39 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmArgs g) {
         }
         // refill the slot just consumed, into the same registers (a separate
         // destination would need a copy, i.e. a wait, at the loop's back edge)
-#ifdef PJ_NT
-        bfrag[j] = __builtin_nontemporal_load((const bf16x8_t*)(lb + 32 * j));
-#else
-        bfrag[j] = *(const bf16x8_t*)(lb + 32 * j);
-#endif
+        bfrag[j] = *(const bf16x8_t*)(lb + 512 * j);
         // keep each step's load here: the scheduler would otherwise sink all
         // PF loads to the end of the block and drain the ring
         __builtin_amdgcn_sched_barrier(0);
       }
     }
     cur = nxt;
-    // C lane (gq, n): rows 16mb + 4gq + i of the tile, column t*64 + 16*wave + n
-    const int col = t * PJ_TN + 16 * wave + n;
-    if (col < g.N) {
-      float* C = g.C + ((size_t)grp * g.ksplit + ks) * (size_t)g.M * g.N + col;
+    // C lane (gq, n): rows 16mb + 4gq + i of the tile, column 64t + 16 wave + n (< N: N % 64 == 0)
+    float* C = g.C + ((size_t)grp * g.ksplit + ks) * (size_t)g.M * g.N + t * PJ_TN + 16 * wave + n;
 #pragma unroll
-      for (int mb = 0; mb < TM / 16; ++mb)
+    for (int mb = 0; mb < TM / 16; ++mb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int m = m0 + 16 * mb + 4 * gq + i;
-          if (m < g.M) C[(size_t)m * g.N] = acc[mb][i];
-        }
-    }
+      for (int i = 0; i < 4; ++i) {
+        const int m = m0 + 16 * mb + 4 * gq + i;
+        if (m < g.M) C[(size_t)m * g.N] = acc[mb][i];
+      }
   }
-  WAIT_VMCNT(0);  // the last ring of loads (re-reads of a valid row) before exit
+  WAIT_VMCNT(0);  // the last ring of loads before exit
+}
+
+// Packing: one thread per 16-byte group of eight k-consecutive values.
+__global__ __launch_bounds__(256) void pack_weights_kernel(const bf16* W, bf16* P, int N, int K, size_t total) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;  // packed 16-byte group
+  if (i >= total) return;
+  const int kch = K >> 9;
+  const int lane = (int)(i & 63), j = (int)((i >> 6) & 15);
+  const size_t blk = i >> 10;  // (g, c, h) block
+  const int h = (int)(blk % kch);
+  const size_t gc = blk / kch;  // g * N/16 + c
+  const size_t g = gc / (N >> 4);
+  const int c = (int)(gc - g * (N >> 4));
+  const int col = 16 * c + (lane & 15), k = 512 * h + 32 * j + 8 * (lane >> 4);
+  *(uint4*)(P + 8 * i) = *(const uint4*)(W + (g * N + col) * (size_t)K + k);
 }
 
 struct FinishArgs {
@@ -275,31 +296,44 @@ namespace csa_host {
 using namespace csa;
 
 struct GemmPlan {
-  int tm, kc, ksplit, mtiles, ntiles, gx;
+  int tm, kc, ksplit, mtiles, ntiles, tpw, gx;
 };
 
 // Tile plan of one (grouped) product, shared by the workspace-size query and
-// the launch.  TM = 32 rows when M <= 32 (decode), else 64.  KC = 1024 when
-// TM = 32 and the problem has enough (tile, split) units to fill the chip at
-// that split, else 512; the A slab then takes <= 64 KiB of LDS (two
-// workgroups per CU).  About 1024 workgroups are launched; each walks the
-// column tiles left to it (the same number for every workgroup where the
-// tile count allows).
+// the launch.  TM = 32 rows when M <= 32 (decode), else 64.  For each K split
+// width KC in {512, 1024, 1536, 2048} (A slab <= 128 KiB of LDS) the column
+// tiles of every (split, row tile, group) are dealt out in contiguous ranges
+// of tpw tiles so that at most one workgroup per CU is needed; the KC with
+// the least estimated per-CU traffic (busiest CU's weight bytes, fp32
+// partials written and read, A slab copies at half weight) wins, the larger
+// KC on ties.  N % 64 == 0 and K % 512 == 0.
 GemmPlan gemm_plan(int groups, int M, int N, int K) {
-  GemmPlan p;
-  p.tm = M <= 32 ? 32 : 64;
-  p.mtiles = (M + p.tm - 1) / p.tm;
-  p.ntiles = (N + PJ_TN - 1) / PJ_TN;
-  const long units1k = (long)p.ntiles * groups * p.mtiles * ((K + 1023) / 1024);
-  p.kc = (p.tm == 32 && K >= 1024 && units1k >= 512) ? 1024 : 512;
-  p.ksplit = (K + p.kc - 1) / p.kc;
-  const long per = (long)p.ksplit * p.mtiles * groups;
-  long gx = (1024 + per - 1) / per;
-  if (gx > p.ntiles) gx = p.ntiles;
-  if (gx < 1) gx = 1;
-  const long tpw = (p.ntiles + gx - 1) / gx;  // tiles per workgroup; then spread them evenly
-  p.gx = (int)((p.ntiles + tpw - 1) / tpw);
-  return p;
+  GemmPlan best{};
+  double best_cost = 0;
+  const int tm = M <= 32 ? 32 : 64;
+  const int mtiles = (M + tm - 1) / tm, ntiles = N / PJ_TN;
+  const int kc_max = tm == 32 ? 2048 : 1024;
+  for (int kc = 512; kc <= kc_max; kc += 512) {
+    const int kce = kc < K ? kc : K;
+    const int ksplit = (K + kce - 1) / kce;
+    const long upc = (long)ksplit * mtiles * groups;  // workgroup rows
+    long cols = PJ_CUS / upc;                          // workgroups per row within one CU round
+    if (cols < 1) cols = 1;
+    int tpw = (int)((ntiles + cols - 1) / cols);
+    const int gx = (ntiles + tpw - 1) / tpw;
+    const long wgs = (long)gx * upc;
+    const long rounds = (wgs + PJ_CUS - 1) / PJ_CUS;
+    const double stream = (double)rounds * tpw * PJ_TN * kce * 2;
+    const double part = (double)groups * ksplit * M * N * 8 / PJ_CUS;
+    const double aslab = (double)rounds * tm * kce;
+    const double cost = stream + part + aslab;
+    if (kc == 512 || cost <= best_cost) {
+      best = GemmPlan{tm, kce, ksplit, mtiles, ntiles, tpw, gx};
+      best_cost = cost;
+    }
+    if (kce == K) break;
+  }
+  return best;
 }
 
 size_t gemm_partial_bytes(int groups, int M, int N, int K) {
@@ -307,12 +341,13 @@ size_t gemm_partial_bytes(int groups, int M, int N, int K) {
   return (size_t)groups * p.ksplit * M * N * sizeof(float);
 }
 
-// K must be a multiple of 512 (every split then holds whole 512-dim chunks).
-hipError_t launch_gemm_nt(const void* A, const void* Bw, float* C, int groups, int M, int N, int K, int lda, int ldb,
-                          long sa, long sb, int* ksplit_out, hipStream_t st) {
+// Bp: packed weights (pack_weights); N % 64 == 0, K % 512 == 0.
+hipError_t launch_gemm_nt(const void* A, const void* Bp, float* C, int groups, int M, int N, int K, int lda, long sa,
+                          long sb, int* ksplit_out, hipStream_t st) {
   const GemmPlan p = gemm_plan(groups, M, N, K);
-  GemmArgs g{(const bf16*)A, (const bf16*)Bw, C, M, N, K, lda, ldb, sa, sb, p.kc, p.ksplit, p.ntiles};
-  const dim3 grid((unsigned)p.gx, (unsigned)(p.ksplit * p.mtiles), (unsigned)groups);
+  GemmArgs g{(const bf16*)A, (const bf16*)Bp, C, M, N, K, lda, sa, sb, p.kc, p.ksplit, p.ntiles, p.tpw, p.gx, p.mtiles,
+             groups};
+  const dim3 grid((unsigned)(p.gx * p.ksplit * p.mtiles * groups));
   const size_t lds = (size_t)p.tm * pj_row_bytes(p.kc);
   if (ksplit_out) *ksplit_out = p.ksplit;
   // A slabs above 64 KiB need the dynamic-LDS limit raised, once per device
@@ -323,17 +358,25 @@ hipError_t launch_gemm_nt(const void* A, const void* Bw, float* C, int groups, i
   const unsigned long long bit = 1ull << (dev & 63);
   if (!(raised.load() & bit)) {
     e = hipFuncSetAttribute((const void*)gemm_nt_kernel<32>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)(32 * pj_row_bytes(1024)));
+                            (int)(32 * pj_row_bytes(2048)));
     if (e == hipSuccess)
       e = hipFuncSetAttribute((const void*)gemm_nt_kernel<64>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              (int)(64 * pj_row_bytes(512)));
+                              (int)(64 * pj_row_bytes(1024)));
     if (e != hipSuccess) return e;
     raised.fetch_or(bit);
   }
   if (p.tm == 32)
-    hipLaunchKernelGGL(gemm_nt_kernel<32>, grid, dim3(256), lds, st, g);
+    hipLaunchKernelGGL(gemm_nt_kernel<32>, grid, dim3(64 * PJ_NW), lds, st, g);
   else
-    hipLaunchKernelGGL(gemm_nt_kernel<64>, grid, dim3(256), lds, st, g);
+    hipLaunchKernelGGL(gemm_nt_kernel<64>, grid, dim3(64 * PJ_NW), lds, st, g);
+  return hipGetLastError();
+}
+
+// groups x [N][K] -> packed; N % 16 == 0, K % 512 == 0.
+hipError_t launch_pack_weights(const void* W, void* P, int groups, int N, int K, hipStream_t st) {
+  const size_t total = (size_t)groups * N * (size_t)K / 8;
+  hipLaunchKernelGGL(pack_weights_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, (const bf16*)W,
+                     (bf16*)P, N, K, total);
   return hipGetLastError();
 }
 
@@ -342,8 +385,8 @@ hipError_t launch_gemm_nt(const void* A, const void* Bw, float* C, int groups, i
 hipError_t launch_rows_finish(const float* part, void* out, const float* gamma, const int32_t* pos, int M, int ncols,
                               int gcols, int seg, int ksplit, int norm, int rope_dim, int S, float eps, float base,
                               hipStream_t st) {
-  int spw = 1;  // segments per workgroup: up to 1024 columns
-  while (2 * spw * seg <= 1024 && (ncols / seg) % (2 * spw) == 0) spw *= 2;
+  int spw = 1;  // segments per workgroup: up to 2048 columns (FN_PASS passes)
+  while (2 * spw * seg <= 1024 * FN_PASS && (ncols / seg) % (2 * spw) == 0) spw *= 2;
   FinishArgs f{part, (bf16*)out, gamma, pos, M, ncols, gcols, seg, spw, ksplit, norm, rope_dim, S, eps,
                std::log2((double)base)};
   hipLaunchKernelGGL(rows_finish_kernel, dim3((unsigned)(ncols / (seg * spw)), (unsigned)M), dim3(FN_THREADS), 0, st,

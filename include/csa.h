@@ -252,6 +252,18 @@ int swa_attn(const void* q, const void* win_kv, const int32_t* win_pos0, const f
              int W_cap, int window, float softmax_scale, float rope_base, int dtype, csa_stream_t stream);
 
 /*
+ * csa_pack_weights -- the weight layout read by csa_q_proj and csa_o_proj.
+ * w: groups x [N][K] bf16 row-major (a weight applied as x W^T); packed:
+ * groups x N*K bf16, written, not overlapping w.  Group g, block (c, h) of
+ * 16 columns x 512 dims sits at element g*N*K + (c*K/512 + h) * 8192 and holds,
+ * for k-step j in [0, 16) and lane l in [0, 64), the eight values
+ * W[16c + l%16][512h + 32j + 8*(l/16) + e] (e in [0, 8)) at (64j + l)*8 + e.
+ * A pure permutation: packing is exact.  Done once per weight, off the hot path.
+ * Requires: N a positive multiple of 64, K of 512.
+ */
+int csa_pack_weights(const void* w, void* packed, int groups, int N, int K, csa_stream_t stream);
+
+/*
  * csa_q_proj -- low-rank query projection, [P1] "低秩 Q：两次矩阵乘法接起来":
  *   qr = RMSNorm(x wq_a^T) with gain gamma_q;  q = qr wq_b^T as [M, H, D];
  *   each head divided by sqrt(mean over D of q^2 + eps); RoPE (the pair
@@ -259,8 +271,9 @@ int swa_attn(const void* q, const void* win_kv, const int32_t* win_pos0, const f
  *   head at the row's position.  Rows are M = B*S tokens, sequence-major:
  *   row m is token m % S of sequence m / S, at position pos[m / S] + m % S.
  *
- * x: [M, d_model] bf16; wq_a: [q_rank, d_model] bf16; gamma_q: [q_rank]
- *   fp32; wq_b: [H*D, q_rank] bf16; pos: [B] device int32.
+ * x: [M, d_model] bf16; wq_a: [q_rank, d_model] bf16 and wq_b: [H*D, q_rank]
+ *   bf16, both packed by csa_pack_weights (groups = 1); gamma_q: [q_rank]
+ *   fp32; pos: [B] device int32.
  * qr: [M, q_rank] bf16, written (it is also the second product's input);
  * q: [M, H, D] bf16, written: the attention's query layout.
  * Products accumulate in fp32; qr and q are rounded to bf16 once.
@@ -283,7 +296,8 @@ int csa_q_proj(const void* x, const void* wq_a, const float* gamma_q, const void
  *   y = r (flattened group-major) wo_b^T.
  *
  * o: [M, H, D] bf16 (attention output); wo_a: [groups, o_rank, H/groups*D]
- *   bf16; wo_b: [d_model, groups*o_rank] bf16.
+ *   bf16 packed by csa_pack_weights(groups, o_rank, H/groups*D); wo_b:
+ *   [d_model, groups*o_rank] bf16 packed with groups = 1.
  * r: [M, groups*o_rank] bf16, written; y: [M, d_model] bf16, written.
  * Products accumulate in fp32; r and y are rounded to bf16 once.
  * workspace: csa_o_proj_workspace_size(M, ...) bytes of fp32 partials, as

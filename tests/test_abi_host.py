@@ -157,3 +157,11 @@ def test_o_proj_validation(lib):
     need = lib.csa_o_proj_workspace_size(32, 128, 512, 16, 1024, 7168)
     assert need >= 16 * 32 * 1024 * 4
     assert op(nws=need - 1) == CSA_ERR_WORKSPACE
+
+
+def test_pack_weights_validation(lib):
+    assert lib.csa_pack_weights(None, P, 1, 64, 512, None) == CSA_ERR_NULL
+    assert lib.csa_pack_weights(P, MIS, 1, 64, 512, None) == CSA_ERR_ALIGN
+    assert lib.csa_pack_weights(P, P, 1, 96, 512, None) == CSA_ERR_SHAPE       # N % 64
+    assert lib.csa_pack_weights(P, P, 1, 64, 768, None) == CSA_ERR_SHAPE       # K % 512
+    assert lib.csa_pack_weights(P, ctypes.c_void_p(4096 + 1024), 1, 64, 512, None) == CSA_ERR_SHAPE   # overlap

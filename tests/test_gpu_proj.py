@@ -18,10 +18,16 @@ from parity import TOL, assert_close, to_np
 pytestmark = pytest.mark.gpu
 
 
+def _packed(dev):
+    """The weights in the layout the projections read (packed on the GPU)."""
+    return {k: K.csa_pack_weights(dev[k]) for k in ("wq_a", "wq_b", "wo_a", "wo_b")}
+
+
 def _run_q(dev, ps):
     qr = torch.empty(ps.M, ps.q_rank, dtype=torch.bfloat16, device="cuda")
     q = torch.empty(ps.M, ps.H, ps.D, dtype=torch.bfloat16, device="cuda")
-    K.csa_q_proj(dev["x"], dev["wq_a"], dev["gamma_q"], dev["wq_b"], dev["pos"], qr, q, B=ps.B, S=ps.S,
+    pw = _packed(dev)
+    K.csa_q_proj(dev["x"], pw["wq_a"], dev["gamma_q"], pw["wq_b"], dev["pos"], qr, q, B=ps.B, S=ps.S,
                  rope_dim=ps.rope)
     torch.cuda.synchronize()
     return to_np(qr), to_np(q)
@@ -30,7 +36,8 @@ def _run_q(dev, ps):
 def _run_o(dev, ps):
     r = torch.empty(ps.M, ps.groups * ps.o_rank, dtype=torch.bfloat16, device="cuda")
     y = torch.empty(ps.M, ps.d_model, dtype=torch.bfloat16, device="cuda")
-    K.csa_o_proj(dev["o"], dev["wo_a"], dev["wo_b"], r, y, groups=ps.groups)
+    pw = _packed(dev)
+    K.csa_o_proj(dev["o"], pw["wo_a"], pw["wo_b"], r, y, groups=ps.groups)
     torch.cuda.synchronize()
     return to_np(r), to_np(y)
 
@@ -100,3 +107,16 @@ def test_projections_repeatable():
     a = _run_q(dev, ps)[1], _run_o(dev, ps)[1]
     b = _run_q(dev, ps)[1], _run_o(dev, ps)[1]
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_pack_weights_is_the_documented_permutation():
+    """Packed element (g, c, h, j, l, e) is W[g][16c + l%16][512h + 32j + 8(l/16) + e],
+    bit for bit; checked with NumPy reshapes on the host."""
+    rng = np.random.default_rng(12)
+    G, N, Kd = 3, 128, 1024
+    w = rng.integers(0, 1 << 16, size=(G, N, Kd), dtype=np.uint16)
+    dev = torch.from_numpy(w.view(np.int16)).cuda().view(torch.bfloat16)
+    got = K.csa_pack_weights(dev).cpu().view(torch.int16).numpy().view(np.uint16).reshape(-1)
+    # W[g, 16c + n, 512h + 32j + 8q + e] -> order (g, c, h, j, q, n, e)
+    ref = w.reshape(G, N // 16, 16, Kd // 512, 16, 4, 8).transpose(0, 1, 3, 4, 5, 2, 6).reshape(-1)
+    assert np.array_equal(got, ref)

@@ -222,6 +222,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="wall time of the CPU oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-projections", action="store_true", help="skip the Q/O projection measurement")
+    ap.add_argument("--projections-only", action="store_true",
+                    help="only measure the Q/O projections at decode (B=32) and print their JSON")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes (HBM counter calibration) and exit")
     args = ap.parse_args()
@@ -231,6 +233,9 @@ def main():
     if args.gpus != 1:
         print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1"}))
         sys.exit(2)
+    if args.projections_only:
+        print(json.dumps({"projections": measure_projections(32, iters=max(1, args.steps))}))
+        return
 
     import torch
     from compressed_sparse_attention_c4a_amd import binding as K

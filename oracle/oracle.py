@@ -173,8 +173,11 @@ def attn(q, cmp_cache, win_kv, sink, q_pos, *, topk_idx=None, ratio=4, win_pos0=
          rope_dim=64, scale=None, rope_base=10000.0):
     """Sparse (topk_idx given) or dense (topk_idx None: all visible entries) MQA with sink.
 
+    FP8 rows (uint8 [..., 640], see quantize_rows_fp8) are read as their
+    dequantised values.
+
     Returns (out f64 [B,S,H,D], lse [B,S,H], ncand [B,S])."""
-    q, cmp_cache, win_kv = _c(q), _c(cmp_cache), _c(win_kv)
+    q, cmp_cache, win_kv = _c(q), _c(widen_kv(cmp_cache)), _c(widen_kv(win_kv))
     B, S, H, D = q.shape
     N_cap = cmp_cache.shape[1]
     W_cap = win_kv.shape[1]
@@ -353,11 +356,23 @@ def round_bf16(values64) -> np.ndarray:
     return (y32.view(np.uint32) >> 16).astype(np.uint16)
 
 
+def is_fp8_rows(a) -> bool:
+    return a is not None and a.dtype == np.uint8 and a.shape[-1] == FP8_ROW_BYTES
+
+
+def widen_kv(a):
+    """Cache or window rows as stored -> values the attention reads (FP8 rows
+    dequantised, other types unchanged)."""
+    return dequantize_rows_fp8(a) if is_fp8_rows(a) else a
+
+
 def _store_like(raw: np.ndarray, values64: np.ndarray) -> np.ndarray:
     """Round fp64 values once to the storage type of ``raw``: bf16 bits by
-    round_bf16, fp32 by numpy's nearest-even cast, fp64 unchanged.  The caches
-    are bf16 in the bf16 configurations, so the attention and index stages
-    read entries rounded this way."""
+    round_bf16, fp32 by numpy's nearest-even cast, fp64 unchanged, FP8 rows by
+    quantize_rows_fp8.  The caches are bf16 in the bf16 configurations, so the
+    attention and index stages read entries rounded this way."""
+    if is_fp8_rows(raw):
+        return quantize_rows_fp8(values64)
     if raw.dtype == np.uint16:
         return round_bf16(values64)
     if raw.dtype == np.float32:
@@ -366,7 +381,7 @@ def _store_like(raw: np.ndarray, values64: np.ndarray) -> np.ndarray:
 
 
 def widen(raw: np.ndarray) -> np.ndarray:
-    return _f64(raw)
+    return dequantize_rows_fp8(raw) if is_fp8_rows(raw) else _f64(raw)
 
 
 def compress_into(raw_cache, kv_state, score_state, gamma, pos0, ratio, overlap, rope_dim, eps=1e-6,
@@ -478,3 +493,102 @@ def o_proj(o, wo_a, wo_b, *, groups: int, store=None):
         r = _f64(round_bf16(r))
     y = r.reshape(M, -1) @ _f64(wo_b).T
     return y, r
+
+
+# --------------------------------------------------------------------------
+# FP8 cache rows ("图解DeepSeek V4：详细计算流程解析" 2, CSA模块: the rope_head_dim
+# part of a KV row is rotated, the rest is quantised; the page gives no format)
+# --------------------------------------------------------------------------
+# Reading: OCP FP8 E4M3 (1 sign, 4 exponent bits with bias 7, 3 mantissa bits,
+# largest finite 448, codes 0x7F/0xFF NaN, no infinity) for the first D - rope
+# dims, one power-of-two scale 2^k per 64-dim block (k the smallest integer with
+# max|x| <= 448 * 2^k, k = 0 for an all-zero block, clamped to [-120, 120]),
+# values rounded to the nearest E4M3 value of x / 2^k, ties to the even code;
+# the rope dims kept as bf16.  Row of D = 512, rope = 64: bytes [0, 448) codes,
+# [448, 576) the 64 bf16 rope dims, [576, 583) the 7 exponents k as int8,
+# [583, 640) zero.  Dequantised value: E4M3 value x 2^k, exact in bf16.
+FP8_ROW_BYTES = 640
+FP8_BLOCK = 64
+
+
+def e4m3_value(code) -> np.ndarray:
+    """The value of each E4M3 code (fp64; NaN for 0x7F and 0xFF)."""
+    c = np.asarray(code).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 15
+    m = (c & 7).astype(np.float64)
+    val = np.where(e == 0, m * 2.0 ** -9, (8.0 + m) * np.exp2(e.astype(np.float64) - 10.0))
+    val = np.where((c & 0x7F) == 0x7F, np.nan, val)
+    return sign * val
+
+
+def e4m3_rne(v) -> np.ndarray:
+    """E4M3 codes of values |v| <= 448: nearest representable value, ties to
+    the even code.  Below 2^-6 the spacing is 2^-9 (subnormals); above, a
+    value in [2^e, 2^(e+1)) has spacing 2^(e-3)."""
+    v = np.asarray(v, dtype=np.float64)
+    if np.any(np.abs(v) > 448.0) or np.any(np.isnan(v)):
+        raise ValueError("e4m3_rne takes finite values of magnitude <= 448")
+    a = np.abs(v)
+    sign = (np.signbit(v)).astype(np.int64) << 7
+    sub = a < 2.0 ** -6
+    # subnormal codes 0..8 (8 is the smallest normal, 2^-6)
+    code_sub = np.rint(a * 512.0).astype(np.int64)
+    _, E = np.frexp(np.where(sub, 1.0, a))          # a = f 2^E, f in [0.5, 1)
+    e = E - 1                                         # a in [2^e, 2^(e+1))
+    mant = np.rint((np.ldexp(np.where(sub, 1.0, a), -e) - 1.0) * 8.0).astype(np.int64)
+    carry = mant == 8
+    e = np.where(carry, e + 1, e)
+    mant = np.where(carry, 0, mant)
+    code_norm = ((e + 7) << 3) | mant
+    code = np.where(sub, code_sub, code_norm)
+    return (sign | code).astype(np.uint8)
+
+
+def fp8_block_exp(amax) -> np.ndarray:
+    """Smallest integer k with amax <= 448 * 2^k (0 for amax == 0), clamped to
+    [-120, 120].  With amax in [2^(E-1), 2^E): 448 * 2^(E-10) = 0.4375 * 2^E
+    is too small and 448 * 2^(E-8) = 1.75 * 2^E always enough, so k is E - 9
+    when amax <= 448 * 2^(E-9) (= 0.875 * 2^E) and E - 8 otherwise."""
+    amax = np.asarray(amax, dtype=np.float64)
+    _, E = np.frexp(np.where(amax > 0, amax, 1.0))
+    k = np.where(amax <= np.ldexp(448.0, E - 9), E - 9, E - 8)
+    k = np.where(amax > 0, k, 0)
+    return np.clip(k, -120, 120).astype(np.int64)
+
+
+def quantize_rows_fp8(values, rope_dim: int = 64, decide_in_float32: bool = True) -> np.ndarray:
+    """FP8 rows (uint8 [..., 640]) of D = 512 values per row (see the reading
+    above).  With decide_in_float32 the values are first rounded to float32,
+    the precision in which the kernels hold them when they quantise."""
+    x = np.asarray(values, dtype=np.float64)
+    if decide_in_float32:
+        x = x.astype(np.float32).astype(np.float64)
+    D = x.shape[-1]
+    if D != 512 or rope_dim != 64:
+        raise ValueError("FP8 rows are defined for D = 512, rope_dim = 64")
+    lead = x.shape[:-1]
+    x = x.reshape(-1, D)
+    nq = D - rope_dim
+    blocks = x[:, :nq].reshape(-1, nq // FP8_BLOCK, FP8_BLOCK)
+    k = fp8_block_exp(np.max(np.abs(blocks), axis=-1))             # [R, 7]
+    codes = e4m3_rne(np.ldexp(blocks, -k[..., None])).reshape(-1, nq)
+    out = np.zeros((x.shape[0], FP8_ROW_BYTES), dtype=np.uint8)
+    out[:, :nq] = codes
+    out[:, nq:nq + 2 * rope_dim] = round_bf16(x[:, nq:]).view(np.uint8).reshape(-1, 2 * rope_dim)
+    out[:, nq + 2 * rope_dim:nq + 2 * rope_dim + nq // FP8_BLOCK] = k.astype(np.int8).view(np.uint8)
+    return out.reshape(lead + (FP8_ROW_BYTES,))
+
+
+def dequantize_rows_fp8(rows, rope_dim: int = 64) -> np.ndarray:
+    """fp64 values [..., 512] of FP8 rows."""
+    r = np.asarray(rows, dtype=np.uint8)
+    lead = r.shape[:-1]
+    r = r.reshape(-1, FP8_ROW_BYTES)
+    nq = 512 - rope_dim
+    k = r[:, nq + 2 * rope_dim:nq + 2 * rope_dim + nq // FP8_BLOCK].view(np.int8).astype(np.int64)
+    vals = e4m3_value(r[:, :nq]).reshape(-1, nq // FP8_BLOCK, FP8_BLOCK)
+    out = np.empty((r.shape[0], 512), dtype=np.float64)
+    out[:, :nq] = np.ldexp(vals, k[..., None]).reshape(-1, nq)
+    out[:, nq:] = _f64(np.ascontiguousarray(r[:, nq:nq + 2 * rope_dim]).view(np.uint16))
+    return out.reshape(lead + (512,))

@@ -15,7 +15,8 @@ from concurrent.futures import ThreadPoolExecutor
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-PINS = ["tests/test_oracle_pins.py", "tests/test_oracle_bf16_pins.py", "tests/test_oracle_proj_pins.py"]
+PINS = ["tests/test_oracle_pins.py", "tests/test_oracle_bf16_pins.py", "tests/test_oracle_proj_pins.py",
+        "tests/test_oracle_fp8_pins.py"]
 
 # (name, file, original text, mutated text): the original must occur in the file
 MUTANTS = [
@@ -66,6 +67,15 @@ MUTANTS = [
      "r[:, g, :] = (og[:, g, :] @ Wa[g].reshape(Wa.shape[2], Wa.shape[1]))"),
     ("O store skipped", "oracle/oracle.py", "        r = _f64(round_bf16(r))\n", "        pass\n"),
     ("Q store skipped", "oracle/oracle.py", "        qr = _f64(round_bf16(qr))\n", "        pass\n"),
+    ("E4M3 subnormal spacing 2^-10", "oracle/oracle.py", "code_sub = np.rint(a * 512.0)", "code_sub = np.rint(a * 1024.0)"),
+    ("E4M3 ties away from zero", "oracle/oracle.py", "mant = np.rint((np.ldexp(np.where(sub, 1.0, a), -e) - 1.0) * 8.0)",
+     "mant = np.floor((np.ldexp(np.where(sub, 1.0, a), -e) - 1.0) * 8.0 + 0.5)"),
+    ("E4M3 decode bias 8", "oracle/oracle.py", "np.exp2(e.astype(np.float64) - 10.0)", "np.exp2(e.astype(np.float64) - 11.0)"),
+    ("FP8 block exponent one too large", "oracle/oracle.py", "np.where(amax <= np.ldexp(448.0, E - 9), E - 9, E - 8)",
+     "np.where(amax <= np.ldexp(448.0, E - 9), E - 8, E - 7)"),
+    ("FP8 rope dims truncated", "oracle/oracle.py", "out[:, nq:nq + 2 * rope_dim] = round_bf16(x[:, nq:])",
+     "out[:, nq:nq + 2 * rope_dim] = (x[:, nq:].astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)"),
+    ("FP8 decision in fp64", "oracle/oracle.py", "        x = x.astype(np.float32).astype(np.float64)\n", "        x = x\n"),
 ]
 
 

@@ -55,6 +55,8 @@ def load() -> ctypes.CDLL:
                       i32, vp], i32),
         "swa_attn": ([vp, vp, vp, vp, vp, vp, vp, vp, sz, i32, i32, i32, i32, i32, i32, i32, f32, f32, i32, vp], i32),
         "csa_pack_weights": ([vp, vp, i32, i32, i32, vp], i32),
+        "csa_quantize_rows": ([vp, vp, ctypes.c_long, i32, i32, vp], i32),
+        "csa_dequantize_rows": ([vp, vp, ctypes.c_long, i32, i32, vp], i32),
         "csa_q_proj_workspace_size": ([i32, i32, i32, i32, i32], sz),
         "csa_q_proj": ([vp, vp, vp, vp, vp, vp, vp, vp, sz, i32, i32, i32, i32, i32, i32, i32, f32, f32, vp], i32),
         "csa_o_proj_workspace_size": ([i32, i32, i32, i32, i32, i32], sz),
@@ -312,6 +314,37 @@ def swa_attn(q, win_kv, win_pos0, sink, q_pos, out, lse=None, *, rope_dim: int, 
             _ptr(lse, torch.float32, "lse"), _ptr(workspace, None, "workspace"), ws_bytes, B, S, H, D, rope_dim, W_cap,
             window, scale, rope_base, _dtype_code(q), _stream(stream))
     return _run("swa_attn", args, prepare, keep=(workspace,))
+
+
+FP8_ROW_BYTES = 640
+
+
+def csa_quantize_rows(src, dst=None, *, stream=None, prepare: bool = False):
+    """bf16 KV rows [..., 512] -> FP8 rows uint8 [..., 640] (see include/csa.h)."""
+    if src.shape[-1] != 512:
+        raise ValueError("FP8 rows hold 512 values")
+    rows = src.numel() // 512
+    if dst is None:
+        dst = torch.empty(src.shape[:-1] + (FP8_ROW_BYTES,), dtype=torch.uint8, device=src.device)
+    if rows == 0:
+        return dst
+    args = (_ptr(src, torch.bfloat16, "src"), _ptr(dst, torch.uint8, "dst"), rows, 512, 64, _stream(stream))
+    _run("csa_quantize_rows", args, prepare)
+    return dst
+
+
+def csa_dequantize_rows(src, dst=None, *, stream=None, prepare: bool = False):
+    """FP8 rows uint8 [..., 640] -> bf16 [..., 512] (exact)."""
+    if src.shape[-1] != FP8_ROW_BYTES:
+        raise ValueError("FP8 rows are 640 bytes")
+    rows = src.numel() // FP8_ROW_BYTES
+    if dst is None:
+        dst = torch.empty(src.shape[:-1] + (512,), dtype=torch.bfloat16, device=src.device)
+    if rows == 0:
+        return dst
+    args = (_ptr(src, torch.uint8, "src"), _ptr(dst, torch.bfloat16, "dst"), rows, 512, 64, _stream(stream))
+    _run("csa_dequantize_rows", args, prepare)
+    return dst
 
 
 def csa_pack_weights(w, packed=None, *, stream=None, prepare: bool = False):

@@ -399,6 +399,30 @@ int swa_attn(const void* q, const void* win_kv, const int32_t* win_pos0, const f
                                             rope_base, dtype, (hipStream_t)stream));
 }
 
+// ---- FP8 KV rows -------------------------------------------------------------
+static int check_fp8_rows(const char* fn, const void* src, const void* dst, long rows, int D, int rope_dim,
+                          size_t src_row, size_t dst_row) {
+  REQ_PTR(src);
+  REQ_PTR(dst);
+  REQ(rows >= 0 && rows <= (1L << 32), "%s: rows must be in [0, 2^32]", fn);
+  REQ(D == 512 && rope_dim == 64, "%s: FP8 rows are defined for D = 512 and rope_dim = 64", fn);
+  const char *a = (const char*)src, *b = (const char*)dst;
+  REQ(a + rows * src_row <= b || b + rows * dst_row <= a, "%s: src and dst overlap", fn);
+  return 0;
+}
+
+int csa_quantize_rows(const void* src, void* dst, long rows, int D, int rope_dim, csa_stream_t stream) {
+  const char* fn = "csa_quantize_rows";
+  if (int rc = check_fp8_rows(fn, src, dst, rows, D, rope_dim, 1024, CSA_FP8_ROW_BYTES)) return rc;
+  return launched(fn, csa_host::launch_quantize_rows(src, dst, rows, (hipStream_t)stream));
+}
+
+int csa_dequantize_rows(const void* src, void* dst, long rows, int D, int rope_dim, csa_stream_t stream) {
+  const char* fn = "csa_dequantize_rows";
+  if (int rc = check_fp8_rows(fn, src, dst, rows, D, rope_dim, CSA_FP8_ROW_BYTES, 1024)) return rc;
+  return launched(fn, csa_host::launch_dequantize_rows(src, dst, rows, (hipStream_t)stream));
+}
+
 // ---- projections around the attention --------------------------------------
 static size_t max_sz(size_t a, size_t b) { return a > b ? a : b; }
 

@@ -157,6 +157,52 @@ __device__ __forceinline__ void lds_barrier() {
   __asm__ volatile("" ::: "memory");
 }
 
+// ---------------------------------------------------------------------------
+// FP8 KV rows ("图解DeepSeek V4" 2: the non-RoPE part of a KV row is quantised).
+// D = 512 values: bytes [0, 448) OCP E4M3 codes of the first 448 dims, one
+// power-of-two scale 2^k per 64-dim block; [448, 576) the 64 RoPE dims as bf16;
+// [576, 583) the 7 exponents k as int8; [583, 640) zero.
+constexpr int FP8_ROW_BYTES = 640;
+constexpr int FP8_NQ = 448;       // quantised dims
+constexpr int FP8_SCALE_OFF = 576;
+
+// Smallest k with amax <= 448 * 2^k (0 for amax == 0), clamped to [-120, 120].
+// With amax in [2^(E-1), 2^E) the answer is E - 9 when amax <= 448 * 2^(E-9)
+// (= 0.875 * 2^E) and E - 8 otherwise.
+__device__ __forceinline__ int fp8_block_exp(float amax) {
+  if (!(amax > 0.f)) return 0;
+  int E;
+  (void)frexpf(amax, &E);
+  const int k = (amax <= ldexpf(448.f, E - 9)) ? E - 9 : E - 8;
+  return k < -120 ? -120 : (k > 120 ? 120 : k);
+}
+
+// E4M3 code of v (|v| <= 448): the nearest E4M3 value, ties to the even code.
+// Below 2^-6 the spacing is 2^-9 (codes 0..8, 8 being 2^-6); a value in
+// [2^e, 2^(e+1)) rounds its 3 mantissa bits.  The sign bit is v's own.
+__device__ __forceinline__ uint32_t fp8_e4m3_rne(float v) {
+  const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
+  const float a = fabsf(v);
+  if (a < 0.015625f) return sign | (uint32_t)rintf(a * 512.f);
+  int E;
+  (void)frexpf(a, &E);
+  int e = E - 1;
+  int mant = (int)rintf((ldexpf(a, -e) - 1.f) * 8.f);
+  if (mant == 8) {
+    e += 1;
+    mant = 0;
+  }
+  return sign | ((uint32_t)(e + 7) << 3) | (uint32_t)mant;
+}
+
+// bf16 bits of E4M3 code c times 2^k: exact (the value has at most 4
+// significant bits), so the upper half of the fp32 value is the bf16 value.
+__device__ __forceinline__ uint32_t fp8_pair_to_bf16x2(uint32_t two_codes, int k) {
+  const auto f = __builtin_amdgcn_cvt_pk_f32_fp8((int)two_codes, false);  // codes in bits [0, 16)
+  const uint32_t lo = __float_as_uint(ldexpf(f[0], k)) >> 16, hi = __float_as_uint(ldexpf(f[1], k)) >> 16;
+  return lo | (hi << 16);
+}
+
 // Inclusive prefix sum over the 64 lanes of a wave with DPP moves (no LDS
 // round trips): shifts by 1, 2, 4, 8 inside each 16-lane row, then row 15
 // into rows 1 and 3 and lane 31 into rows 2 and 3.
@@ -237,6 +283,8 @@ hipError_t launch_attn(const void* q, const void* cmp, const int32_t* topk_idx, 
                        const int32_t* win_pos0, const float* sink, const int32_t* q_pos, void* out, float* lse,
                        void* ws, int B, int S, int H, int D, int rope_dim, int N_cap, int W_cap, int window,
                        float scale, float base, int dtype, hipStream_t st);
+hipError_t launch_quantize_rows(const void* src, void* dst, long rows, hipStream_t st);
+hipError_t launch_dequantize_rows(const void* src, void* dst, long rows, hipStream_t st);
 size_t gemm_partial_bytes(int groups, int M, int N, int K);
 hipError_t launch_gemm_nt(const void* A, const void* Bp, float* C, int groups, int M, int N, int K, int lda, long sa,
                           long sb, int* ksplit_out, hipStream_t st);

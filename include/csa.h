@@ -55,6 +55,9 @@ typedef struct ihipStream_t* csa_stream_t; /* identical to hipStream_t */
 /* Flags of csa_index_scores / csa_index_topk. */
 #define CSA_INDEX_NO_RELU 1u /* score = sum_h w_h * (q_h . k), without ReLU */
 
+/* FP8 KV rows: bytes per row of D = 512 values (see csa_quantize_rows). */
+#define CSA_FP8_ROW_BYTES 640
+
 int csa_version(void);
 const char* csa_error_string(int code);
 const char* csa_last_error(void); /* detail of the calling thread's last error */
@@ -250,6 +253,27 @@ int hca_attn(const void* q, const void* cmp_cache, const void* win_kv, const int
 int swa_attn(const void* q, const void* win_kv, const int32_t* win_pos0, const float* sink, const int32_t* q_pos,
              void* out, float* lse, void* workspace, size_t workspace_bytes, int B, int S, int H, int D, int rope_dim,
              int W_cap, int window, float softmax_scale, float rope_base, int dtype, csa_stream_t stream);
+
+/*
+ * csa_quantize_rows -- KV rows to the FP8 row format, [P5] §2 (CSA模块): the
+ * rope_head_dim part of a window KV row is rotated, the rest is quantised (the
+ * page states neither format nor granularity; the reading taken):
+ *   bytes [0, 448): OCP FP8 E4M3 codes (bias 7, largest 448, no infinity) of
+ *     dims 0..447 divided by 2^k_b, rounded to nearest, ties to the even code;
+ *   bytes [448, 576): dims 448..511 (the RoPE dims) as bf16, unchanged;
+ *   bytes [576, 583): k_0..k_6 as int8, k_b the smallest integer with
+ *     max over block b (dims 64b..64b+63) of |x| <= 448 * 2^k_b (0 for an
+ *     all-zero block), clamped to [-120, 120]; bytes [583, 640): zero.
+ * A stored value reads back as E4M3 value * 2^k_b, exactly a bf16 value.
+ * src: [rows, 512] bf16; dst: [rows, CSA_FP8_ROW_BYTES] bytes; no overlap.
+ * Requires D == 512 and rope_dim == 64.
+ */
+int csa_quantize_rows(const void* src, void* dst, long rows, int D, int rope_dim, csa_stream_t stream);
+
+/*
+ * csa_dequantize_rows -- FP8 rows back to bf16 [rows, 512] (exact).
+ */
+int csa_dequantize_rows(const void* src, void* dst, long rows, int D, int rope_dim, csa_stream_t stream);
 
 /*
  * csa_pack_weights -- the weight layout read by csa_q_proj and csa_o_proj.

@@ -165,3 +165,12 @@ def test_pack_weights_validation(lib):
     assert lib.csa_pack_weights(P, P, 1, 96, 512, None) == CSA_ERR_SHAPE       # N % 64
     assert lib.csa_pack_weights(P, P, 1, 64, 768, None) == CSA_ERR_SHAPE       # K % 512
     assert lib.csa_pack_weights(P, ctypes.c_void_p(4096 + 1024), 1, 64, 512, None) == CSA_ERR_SHAPE   # overlap
+
+
+def test_fp8_rows_validation(lib):
+    assert lib.csa_quantize_rows(None, P, 4, 512, 64, None) == CSA_ERR_NULL
+    assert lib.csa_quantize_rows(P, MIS, 4, 512, 64, None) == CSA_ERR_ALIGN
+    assert lib.csa_quantize_rows(P, ctypes.c_void_p(1 << 20), 4, 256, 64, None) == CSA_ERR_SHAPE   # D != 512
+    assert lib.csa_quantize_rows(P, ctypes.c_void_p(1 << 20), 4, 512, 32, None) == CSA_ERR_SHAPE   # rope != 64
+    assert lib.csa_dequantize_rows(P, ctypes.c_void_p(4096 + 640), 4, 512, 64, None) == CSA_ERR_SHAPE  # overlap
+    assert lib.csa_quantize_rows(P, ctypes.c_void_p(1 << 20), -1, 512, 64, None) == CSA_ERR_SHAPE

@@ -251,6 +251,22 @@ def csa_compress_index_topk(kv_state, score_state, gamma, cache, idx_kv_state, i
     return _run("csa_compress_index_topk", head + (_ptr(workspace, None, "workspace"), ws_bytes) + tail, prepare)
 
 
+CSA_BF16_KV_FP8 = 2
+
+
+def _kv(q, *rows):
+    """(dtype code, torch dtype of the KV rows): uint8 rows are FP8 rows read
+    with bf16 q (CSA_BF16_KV_FP8); otherwise the rows have q's dtype."""
+    fp8 = [r is not None and r.dtype == torch.uint8 for r in rows]
+    if any(fp8):
+        if not all(f for f, r in zip(fp8, rows) if r is not None):
+            raise TypeError("either all KV rows are FP8 rows (uint8) or none")
+        if q.dtype != torch.bfloat16:
+            raise TypeError("FP8 KV rows are read with a bf16 q")
+        return CSA_BF16_KV_FP8, torch.uint8
+    return _dtype_code(q), q.dtype
+
+
 def csa_attn_workspace_size(B: int, S: int, H: int, D: int, n_cand: int) -> int:
     return load().csa_attn_workspace_size(B, S, H, D, n_cand)
 
@@ -273,11 +289,12 @@ def csa_sparse_attn(q, cmp_cache, topk_idx, win_kv, win_pos0, sink, q_pos, out, 
     if workspace is None:
         workspace = attn_workspace(B, S, H, D, window + k, q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    args = (_ptr(q, q.dtype, "q"), _ptr(cmp_cache, q.dtype, "cmp_cache"), _ptr(topk_idx, torch.int32, "topk_idx"),
-            _ptr(win_kv, q.dtype, "win_kv"), _ptr(win_pos0, torch.int32, "win_pos0"), _ptr(sink, torch.float32, "sink"),
+    code, kvt = _kv(q, cmp_cache, win_kv)
+    args = (_ptr(q, q.dtype, "q"), _ptr(cmp_cache, kvt, "cmp_cache"), _ptr(topk_idx, torch.int32, "topk_idx"),
+            _ptr(win_kv, kvt, "win_kv"), _ptr(win_pos0, torch.int32, "win_pos0"), _ptr(sink, torch.float32, "sink"),
             _ptr(q_pos, torch.int32, "q_pos"), _ptr(out, q.dtype, "out"), _ptr(lse, torch.float32, "lse"),
             _ptr(workspace, None, "workspace"), ws_bytes, B, S, H, D, rope_dim, N_cap, k, W_cap, window, scale,
-            rope_base, _dtype_code(q), _stream(stream))
+            rope_base, code, _stream(stream))
     return _run("csa_sparse_attn", args, prepare, keep=(workspace,))
 
 
@@ -291,10 +308,11 @@ def hca_attn(q, cmp_cache, win_kv, win_pos0, sink, q_pos, out, lse=None, *, rati
     if workspace is None:
         workspace = attn_workspace(B, S, H, D, window + N_cap, q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    args = (_ptr(q, q.dtype, "q"), _ptr(cmp_cache, q.dtype, "cmp_cache"), _ptr(win_kv, q.dtype, "win_kv"),
+    code, kvt = _kv(q, cmp_cache, win_kv)
+    args = (_ptr(q, q.dtype, "q"), _ptr(cmp_cache, kvt, "cmp_cache"), _ptr(win_kv, kvt, "win_kv"),
             _ptr(win_pos0, torch.int32, "win_pos0"), _ptr(sink, torch.float32, "sink"), _ptr(q_pos, torch.int32, "q_pos"),
             _ptr(out, q.dtype, "out"), _ptr(lse, torch.float32, "lse"), _ptr(workspace, None, "workspace"), ws_bytes,
-            B, S, H, D, rope_dim, N_cap, ratio, W_cap, window, scale, rope_base, _dtype_code(q), _stream(stream))
+            B, S, H, D, rope_dim, N_cap, ratio, W_cap, window, scale, rope_base, code, _stream(stream))
     return _run("hca_attn", args, prepare, keep=(workspace,))
 
 
@@ -309,10 +327,11 @@ def swa_attn(q, win_kv, win_pos0, sink, q_pos, out, lse=None, *, rope_dim: int, 
     if workspace is None:
         workspace = attn_workspace(B, S, H, D, window, q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    args = (_ptr(q, q.dtype, "q"), _ptr(win_kv, q.dtype, "win_kv"), _ptr(win_pos0, torch.int32, "win_pos0"),
+    code, kvt = _kv(q, win_kv)
+    args = (_ptr(q, q.dtype, "q"), _ptr(win_kv, kvt, "win_kv"), _ptr(win_pos0, torch.int32, "win_pos0"),
             _ptr(sink, torch.float32, "sink"), _ptr(q_pos, torch.int32, "q_pos"), _ptr(out, q.dtype, "out"),
             _ptr(lse, torch.float32, "lse"), _ptr(workspace, None, "workspace"), ws_bytes, B, S, H, D, rope_dim, W_cap,
-            window, scale, rope_base, _dtype_code(q), _stream(stream))
+            window, scale, rope_base, code, _stream(stream))
     return _run("swa_attn", args, prepare, keep=(workspace,))
 
 

@@ -61,7 +61,14 @@ int launched(const char* fn, hipError_t e) {
 int check_attn_common(const char* fn, const void* q, const void* cmp, const void* win, const int32_t* win_pos0,
                       const float* sink, const int32_t* q_pos, const void* out, const float* lse, int B, int S, int H,
                       int D, int rope_dim, int N_cap, int W_cap, int window, int dtype) {
-  if (int rc = check_dtype(fn, dtype)) return rc;
+  if (dtype == CSA_BF16_KV_FP8) {
+    // FP8 KV rows are read by the MFMA kernel only
+    if (D != 512 || rope_dim != 64 || H % 16 != 0 || window > 1024)
+      return fail(CSA_ERR_UNSUPPORTED, "%s: FP8 KV rows need D = 512, rope_dim = 64, H %% 16 == 0, window <= 1024",
+                  fn);
+  } else if (int rc = check_dtype(fn, dtype)) {
+    return rc;
+  }
   REQ_PTR(q);
   REQ_PTR(win);
   REQ_PTR(sink);
@@ -356,6 +363,7 @@ int csa_sparse_attn(const void* q, const void* cmp_cache, const int32_t* topk_id
     return rc;
   REQ(k >= 0 && k <= 65536, "%s: k must be in [0, 65536]", fn);
   if (k > 0) REQ_PTR(topk_idx);
+  if (dtype == CSA_BF16_KV_FP8 && k > 2048) return fail(CSA_ERR_UNSUPPORTED, "%s: FP8 KV rows need k <= 2048", fn);
   const size_t need = csa_host::attn_workspace_size(B, S, H, D, window + k);
   if (need && (!workspace || workspace_bytes < need))
     return fail(CSA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed (got %zu)", fn, need, workspace_bytes);

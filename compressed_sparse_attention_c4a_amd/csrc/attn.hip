@@ -256,10 +256,16 @@ __device__ __forceinline__ void store_output(const AttnArgs& a, int qi, int h0, 
   }
 }
 
-template <int NHB>
+// KV8: window and compressed rows in the FP8 row format (common.hpp): the O
+// waves load each row of the next tile into VGPRs (lanes 0..39, 16 bytes each)
+// while the tile in LDS is being used, and after its P.V write the tile
+// dequantised into the same bf16 ring layout (exact), before the barrier that
+// publishes it.  Everything else is the bf16 kernel.
+template <int NHB, bool KV8 = false>
 __global__ __launch_bounds__(512) void attn_tile_kernel(AttnArgs a, int n_hg, int nsplit, int total_items,
                                                         float* __restrict__ part) {
   constexpr int HG = 16 * NHB;
+  constexpr int ROWB = KV8 ? FP8_ROW_BYTES : AT_ROWB;  // bytes per window / compressed row
   __shared__ __attribute__((aligned(16))) uint8_t ring[2][AT_TILE_B];
   __shared__ __attribute__((aligned(16))) __bf16 pbuf[HG][AT_PST];
   __shared__ float mbuf[4][NHB][64];   // S waves' tile maxima (rescale path)
@@ -289,8 +295,8 @@ __global__ __launch_bounds__(512) void attn_tile_kernel(AttnArgs a, int n_hg, in
   const int tb = min(nt_all, split * tps);
   const int ntiles = min(nt_all, tb + tps) - tb;
   const int jb0 = tb * AT_TR;  // first candidate slot of this split
-  const char* winb = (const char*)a.win + (size_t)b * a.W_cap * AT_ROWB;
-  const char* cmpb = (const char*)a.cmp + (size_t)b * a.N_cap * AT_ROWB;
+  const char* winb = (const char*)a.win + (size_t)b * a.W_cap * ROWB;
+  const char* cmpb = (const char*)a.cmp + (size_t)b * a.N_cap * ROWB;
 
   // S waves: the HG q rows of the group once into ring stage 1 (first
   // overwritten by the copies of tile 1, after barrier X_0), swizzled like
@@ -378,8 +384,44 @@ __global__ __launch_bounds__(512) void attn_tile_kernel(AttnArgs a, int n_hg, in
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
       const int id = ids[rr];
-      const char* row = id >= 0 ? cmpb + (size_t)(uint32_t)id * AT_ROWB : winb + (size_t)(uint32_t)(-1 - id) * AT_ROWB;
+      const char* row = id >= 0 ? cmpb + (size_t)(uint32_t)id * ROWB : winb + (size_t)(uint32_t)(-1 - id) * ROWB;
       dma16_sbase(row, 16u * (uint32_t)lane, ring[ti & 1] + (16 * w4 + rr) * AT_RS);
+    }
+  };
+  // FP8 rows: the 16 rows this wave copies of tile ti into VGPRs (lane l < 40
+  // holds bytes 16l .. 16l+15 of each row) ...
+  auto load_tile8 = [&](int ti, uint4 (&fr)[16]) {
+    int ids[16];
+    row_ids(ti, ids);
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {
+      const int id = ids[rr];
+      const char* row = id >= 0 ? cmpb + (size_t)(uint32_t)id * ROWB : winb + (size_t)(uint32_t)(-1 - id) * ROWB;
+      if (lane < 40) fr[rr] = *(const uint4*)(row + 16 * lane);
+    }
+  };
+  // ... and their bf16 values into stage ti & 1: lane l < 28 writes dims
+  // 16l .. 16l+15 (block l / 4, exponent byte l / 4 of the row, which lane 36
+  // holds), lanes 28..35 the RoPE dims 448 + 8(l - 28) .. +8 unchanged.
+  auto store_tile8 = [&](int ti, const uint4 (&fr)[16]) {
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {
+      uint8_t* dst = ring[ti & 1] + (16 * w4 + rr) * AT_RS;
+      const uint32_t s0 = (uint32_t)__builtin_amdgcn_readlane((int)fr[rr].x, 36);
+      const uint32_t s1 = (uint32_t)__builtin_amdgcn_readlane((int)fr[rr].y, 36);
+      if (lane < 28) {
+        const int blk = lane >> 2;
+        const int k = (int)(int8_t)(((blk < 4 ? s0 : s1) >> (8 * (blk & 3))) & 0xFFu);
+        const uint4 c = fr[rr];
+        *(uint4*)(dst + 32 * lane) = make_uint4(fp8_pair_to_bf16x2(c.x & 0xFFFFu, k), fp8_pair_to_bf16x2(c.x >> 16, k),
+                                                fp8_pair_to_bf16x2(c.y & 0xFFFFu, k), fp8_pair_to_bf16x2(c.y >> 16, k));
+        *(uint4*)(dst + 32 * lane + 16) = make_uint4(fp8_pair_to_bf16x2(c.z & 0xFFFFu, k),
+                                                     fp8_pair_to_bf16x2(c.z >> 16, k),
+                                                     fp8_pair_to_bf16x2(c.w & 0xFFFFu, k),
+                                                     fp8_pair_to_bf16x2(c.w >> 16, k));
+      } else if (lane < 36) {
+        *(uint4*)(dst + 2 * FP8_NQ + 16 * (lane - 28)) = fr[rr];
+      }
     }
   };
   auto tile_mask = [&](int ti) -> uint64_t {
@@ -506,12 +548,9 @@ __global__ __launch_bounds__(512) void attn_tile_kernel(AttnArgs a, int n_hg, in
     const int d0 = w4 * 128;            // P.V dim slice of this wave
     // transposed reads: rows 32c + 8g + (n >> 2) (+4), dims d0 + 16dt + 4(n & 3)
     const int tr_off = (8 * g + (n >> 2)) * AT_RS + 2 * d0 + 8 * (n & 3);
-    if (ntiles > 0) copy_tile(0);
-    WAIT_VMCNT(0);
-    lds_barrier();  // X_0
-    for (int i = 0; i < ntiles; ++i) {
+    // Y_i (and Y'_i on a rescale), then this tile's P.V into o
+    auto pv_tile = [&](int i) {
       const uint8_t* tile = ring[i & 1];
-      if (i + 1 < ntiles) copy_tile(i + 1);  // into the stage tile i-1 used
       lds_barrier();  // Y_i
       if (fbuf[0] | fbuf[1] | fbuf[2] | fbuf[3]) {
         lds_barrier();  // Y'_i: rescale factors and the new P visible
@@ -543,9 +582,35 @@ __global__ __launch_bounds__(512) void attn_tile_kernel(AttnArgs a, int n_hg, in
           for (int hb = 0; hb < NHB; ++hb) o[dt][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, pf[hb], o[dt][hb], 0, 0, 0);
         }
       }
-      if (i + 1 < ntiles) {
-        WAIT_VMCNT(0);    // this wave's copies of tile i+1 have landed
-        lds_barrier();    // X_i+1
+    };
+    if constexpr (KV8) {
+      // Every iteration of the loop loads the next tile's rows and consumes them,
+      // so no load is pending at the back edge (the compiler would otherwise
+      // wait for all loads before each new one); the last tile is peeled.
+      uint4 fr[16];
+      if (ntiles > 0) {
+        load_tile8(0, fr);
+        store_tile8(0, fr);
+      }
+      lds_barrier();  // X_0
+      for (int i = 0; i + 1 < ntiles; ++i) {
+        load_tile8(i + 1, fr);   // into VGPRs
+        pv_tile(i);
+        store_tile8(i + 1, fr);  // stage (i+1) & 1: tile i-1's, free since X_i
+        lds_barrier();           // X_i+1
+      }
+      if (ntiles > 0) pv_tile(ntiles - 1);
+    } else {
+      if (ntiles > 0) copy_tile(0);
+      WAIT_VMCNT(0);
+      lds_barrier();  // X_0
+      for (int i = 0; i < ntiles; ++i) {
+        if (i + 1 < ntiles) copy_tile(i + 1);  // into the stage tile i-1 used
+        pv_tile(i);
+        if (i + 1 < ntiles) {
+          WAIT_VMCNT(0);  // this wave's copies of tile i+1 have landed
+          lds_barrier();  // X_i+1
+        }
       }
     }
   }
@@ -726,18 +791,30 @@ hipError_t launch_attn(const void* q, const void* cmp, const int32_t* topk_idx, 
   AttnArgs a{q, cmp, topk_idx, win, win_pos0, sink, q_pos, out, lse, dense, S, H, D, rope_dim, N_cap, k, ratio,
              W_cap, window, scale, std::log2((double)base)};
   const long Q = (long)B * S;
-  if (dtype == CSA_BF16 && D == AT_D && H % 16 == 0 && (dense || k <= AT_MAXK) && window <= AT_MAXWIN) {
+  if ((dtype == CSA_BF16 || dtype == CSA_BF16_KV_FP8) && D == AT_D && H % 16 == 0 && (dense || k <= AT_MAXK) &&
+      window <= AT_MAXWIN) {
     const AttnPlan p = attn_plan(Q, H, window + (dense ? N_cap : k));
     float* part = p.nsplit > 1 ? (float*)ws : nullptr;
     const int items = p.total / p.nsplit;
-    if (p.nhb == 2) {
+    if (dtype == CSA_BF16_KV_FP8) {
+      if (p.nhb == 2)
+        hipLaunchKernelGGL((attn_tile_kernel<2, true>), dim3(p.total), dim3(512), 0, st, a, p.n_hg, p.nsplit, p.total,
+                           part);
+      else
+        hipLaunchKernelGGL((attn_tile_kernel<1, true>), dim3(p.total), dim3(512), 0, st, a, p.n_hg, p.nsplit, p.total,
+                           part);
+    } else if (p.nhb == 2) {
       hipLaunchKernelGGL((attn_tile_kernel<2>), dim3(p.total), dim3(512), 0, st, a, p.n_hg, p.nsplit, p.total, part);
-      if (p.nsplit > 1)
-        hipLaunchKernelGGL((attn_merge_kernel<2>), dim3(items * 16), dim3(64), 0, st, a, p.n_hg, p.nsplit, (const uint8_t*)part);
     } else {
       hipLaunchKernelGGL((attn_tile_kernel<1>), dim3(p.total), dim3(512), 0, st, a, p.n_hg, p.nsplit, p.total, part);
-      if (p.nsplit > 1)
-        hipLaunchKernelGGL((attn_merge_kernel<1>), dim3(items * 16), dim3(64), 0, st, a, p.n_hg, p.nsplit, (const uint8_t*)part);
+    }
+    if (p.nsplit > 1) {
+      if (p.nhb == 2)
+        hipLaunchKernelGGL((attn_merge_kernel<2>), dim3(items * 16), dim3(64), 0, st, a, p.n_hg, p.nsplit,
+                           (const uint8_t*)part);
+      else
+        hipLaunchKernelGGL((attn_merge_kernel<1>), dim3(items * 16), dim3(64), 0, st, a, p.n_hg, p.nsplit,
+                           (const uint8_t*)part);
     }
     return hipGetLastError();
   }

@@ -42,6 +42,10 @@ typedef struct ihipStream_t* csa_stream_t; /* identical to hipStream_t */
 
 #define CSA_F32 0
 #define CSA_BF16 1
+/* bf16 activations (q, out, compressor states) with window and compressed KV
+ * rows in the FP8 row format of csa_quantize_rows (attention and compressor
+ * entry points; the index-key cache stays bf16). */
+#define CSA_BF16_KV_FP8 2
 
 #define CSA_OK 0
 #define CSA_ERR_NULL (-1)        /* a required pointer is NULL */
@@ -216,7 +220,11 @@ int csa_compress_index_topk_noalloc(const void* kv_state, const void* score_stat
  * Requires: 1 <= window <= W_cap (ring mode), D <= 512, D even, rope_dim
  *   even <= D, k >= 0.  The MFMA path runs for dtype CSA_BF16, D == 512,
  *   H % 16 == 0, k <= 2048 and window <= 1024; other shapes use a vector-ALU
- *   kernel.
+ *   kernel.  dtype CSA_BF16_KV_FP8: q and out bf16, cmp_cache and win_kv rows
+ *   in the FP8 row format of csa_quantize_rows ([.., CSA_FP8_ROW_BYTES]
+ *   bytes per row), read as their dequantised values; MFMA path only
+ *   (D == 512, rope_dim == 64, H % 16 == 0, k <= 2048, window <= 1024;
+ *   CSA_ERR_UNSUPPORTED otherwise).
  * workspace: csa_attn_workspace_size(B, S, H, D, n_cand) bytes with n_cand =
  *   window + k (csa_sparse_attn) or window + N_cap (hca_attn); 0 means none
  *   is needed and workspace may be NULL.  When small batches split each

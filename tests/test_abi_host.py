@@ -103,7 +103,7 @@ def test_attention_validation(lib):
     assert _attn(lib, D=514) == CSA_ERR_SHAPE
     assert _attn(lib, rope=65) == CSA_ERR_SHAPE
     assert _attn(lib, window=129) == CSA_ERR_SHAPE            # ring window larger than the ring
-    assert _attn(lib, dtype=2) == CSA_ERR_DTYPE
+    assert _attn(lib, dtype=5) == CSA_ERR_DTYPE
     assert lib.hca_attn(P, P, P, None, P, P, P, None, None, 0, 1, 1, 128, 512, 64, 100, 0, 128, 128, 0.04, 10000.0,
                         1, None) == CSA_ERR_SHAPE               # ratio 0
 
@@ -174,3 +174,12 @@ def test_fp8_rows_validation(lib):
     assert lib.csa_quantize_rows(P, ctypes.c_void_p(1 << 20), 4, 512, 32, None) == CSA_ERR_SHAPE   # rope != 64
     assert lib.csa_dequantize_rows(P, ctypes.c_void_p(4096 + 640), 4, 512, 64, None) == CSA_ERR_SHAPE  # overlap
     assert lib.csa_quantize_rows(P, ctypes.c_void_p(1 << 20), -1, 512, 64, None) == CSA_ERR_SHAPE
+
+
+def test_fp8_attention_shapes(lib):
+    CSA_ERR_UNSUPPORTED = -4
+    assert _attn(lib, dtype=2, H=48 + 8) == CSA_ERR_UNSUPPORTED        # H % 16 != 0
+    assert _attn(lib, dtype=2, rope=32) == CSA_ERR_UNSUPPORTED
+    assert _attn(lib, dtype=2, D=256, rope=64) == CSA_ERR_UNSUPPORTED
+    assert _attn(lib, dtype=2, k=4096) == CSA_ERR_UNSUPPORTED
+    assert _attn(lib, dtype=3) == CSA_ERR_DTYPE

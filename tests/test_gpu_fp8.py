@@ -72,3 +72,57 @@ def test_quantize_empty_and_odd_counts(orc):
         assert got.shape == (R, 640)
         if R:
             assert np.array_equal(got, orc.quantize_rows_fp8(orc.widen(bits)))
+
+
+# ---------------------------------------------------------------- attention on FP8 rows
+from test_gpu_attention import VARIANTS, _dev, _inputs, _seed  # noqa: E402
+from parity import TOL, assert_close, to_np  # noqa: E402
+
+
+def _attn(x, cmp, win, dense, window, H, B, S):
+    out = torch.empty((B, S, H, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, S, H), dtype=torch.float32, device="cuda")
+    if dense:
+        K.hca_attn(_dev(x["q"]), cmp, win, _dev(x["win_pos0"]), _dev(x["sink"]), _dev(x["q_pos"]), out, lse,
+                   ratio=4, rope_dim=64, window=window)
+    else:
+        K.csa_sparse_attn(_dev(x["q"]), cmp, _dev(x["topk"]), win, _dev(x["win_pos0"]), _dev(x["sink"]),
+                          _dev(x["q_pos"]), out, lse, rope_dim=64, window=window)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+@pytest.mark.parametrize("name", sorted(VARIANTS))
+@pytest.mark.parametrize("dense", [False, True])
+def test_attention_on_fp8_rows(orc, name, dense):
+    """The FP8-row kernel equals the bf16 kernel on the dequantised rows bit for
+    bit (it stages exactly those values), and the oracle reading FP8 rows."""
+    B, S, H, N_cap, W_cap, k, q_pos, linear, window = VARIANTS[name]
+    x = _inputs(_seed(name) + 7, B, S, H, N_cap, W_cap, k, q_pos, linear)
+    print(f"[fp8] attention {name} dense={dense}", flush=True)
+    cmp8, win8 = K.csa_quantize_rows(_dev(x["cmp"])), K.csa_quantize_rows(_dev(x["win"]))
+    cmp8_h, win8_h = cmp8.cpu().numpy(), win8.cpu().numpy()
+    assert np.array_equal(cmp8_h, orc.quantize_rows_fp8(orc.widen(x["cmp"])))
+    assert np.array_equal(win8_h, orc.quantize_rows_fp8(orc.widen(x["win"])))
+    out8, lse8 = _attn(x, cmp8, win8, dense, window, H, B, S)
+    outd, lsed = _attn(x, K.csa_dequantize_rows(cmp8), K.csa_dequantize_rows(win8), dense, window, H, B, S)
+    assert torch.equal(out8, outd) and torch.equal(lse8, lsed)
+    ref, rlse, _ = orc.attn(x["q"], cmp8_h, win8_h, x["sink"], x["q_pos"], topk_idx=None if dense else x["topk"],
+                            ratio=4, win_pos0=x["win_pos0"], window=window, rope_dim=64)
+    assert_close(to_np(out8), ref, TOL["bf16"], f"fp8 {name} dense={dense}: output")
+    assert_close(lse8.cpu().numpy(), rlse, 1e-3, f"fp8 {name} dense={dense}: lse")
+
+
+def test_swa_on_fp8_rows(orc):
+    B, H, W_cap, window = 3, 128, 256, 256
+    x = _inputs(31, B, 1, H, 1, W_cap, 1, [5000, 40, 0])
+    win8 = K.csa_quantize_rows(_dev(x["win"]))
+    out = torch.empty((B, 1, H, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, 1, H), dtype=torch.float32, device="cuda")
+    K.swa_attn(_dev(x["q"]), win8, None, _dev(x["sink"]), _dev(x["q_pos"]), out, lse, rope_dim=64, window=window)
+    torch.cuda.synchronize()
+    none = np.zeros((B, 0, 640), dtype=np.uint8)
+    ref, rlse, _ = orc.attn(x["q"], none, win8.cpu().numpy(), x["sink"], x["q_pos"],
+                            topk_idx=np.zeros((B, 1, 0), dtype=np.int32), ratio=1, window=window, rope_dim=64)
+    assert_close(to_np(out), ref, TOL["bf16"], "fp8 swa: output")
+    assert_close(lse.cpu().numpy(), rlse, 1e-3, "fp8 swa: lse")

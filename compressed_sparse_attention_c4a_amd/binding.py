@@ -86,6 +86,20 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
 
 
+CSA_BF16_KV_FP8 = 2
+
+
+def _cache(cache, states):
+    """(d, dtype code, torch dtype of the cache) of a compressor's output
+    cache: uint8 [.., 640] rows are FP8 rows of d = 512 written from bf16
+    states (CSA_BF16_KV_FP8); otherwise the cache has the states' dtype."""
+    if cache.dtype == torch.uint8:
+        if cache.shape[-1] != 640 or states.dtype != torch.bfloat16:
+            raise TypeError("an FP8 cache has 640-byte rows and bf16 states")
+        return 512, CSA_BF16_KV_FP8, torch.uint8
+    return cache.shape[-1], _dtype_code(states), states.dtype
+
+
 def _ptr(t: Optional[torch.Tensor], dtype=None, name="tensor"):
     if t is None:
         return None
@@ -147,13 +161,13 @@ def csa_version() -> int:
 def csa_compress(kv_state, score_state, gamma, cache, pos0, *, ratio: int, overlap: bool, rope_dim: int,
                  eps: float = 1e-6, rope_base: float = 10000.0, stream=None, prepare: bool = False):
     B, L, md = kv_state.shape
-    d = cache.shape[-1]
+    d, code, ct = _cache(cache, kv_state)
     if md != (2 if overlap else 1) * d or score_state.shape != kv_state.shape:
         raise ValueError("state width must be (2 if overlap else 1) * d and kv/score shapes must match")
     dt = kv_state.dtype
     args = (_ptr(kv_state, dt, "kv_state"), _ptr(score_state, dt, "score_state"), _ptr(gamma, torch.float32, "gamma"),
-            _ptr(cache, dt, "cache"), _ptr(pos0, torch.int32, "pos0"), B, L, d, rope_dim, ratio, int(overlap),
-            cache.shape[1], eps, rope_base, _dtype_code(kv_state), _stream(stream))
+            _ptr(cache, ct, "cache"), _ptr(pos0, torch.int32, "pos0"), B, L, d, rope_dim, ratio, int(overlap),
+            cache.shape[1], eps, rope_base, code, _stream(stream))
     return _run("csa_compress", args, prepare)
 
 
@@ -161,18 +175,17 @@ def csa_compress_kv_index(kv_state, score_state, gamma, cache, idx_kv_state, idx
                           pos0, *, ratio: int, overlap: bool, rope_dim: int, idx_rope_dim: int, eps: float = 1e-6,
                           rope_base: float = 10000.0, stream=None, prepare: bool = False):
     B, L, md = kv_state.shape
-    d, di = cache.shape[-1], idx_cache.shape[-1]
+    (d, code, ct), di = _cache(cache, kv_state), idx_cache.shape[-1]
     if md != (2 if overlap else 1) * d or score_state.shape != kv_state.shape:
         raise ValueError("state width must be (2 if overlap else 1) * d and kv/score shapes must match")
     if idx_kv_state.shape != (B, L, 2 * di) or idx_score_state.shape != idx_kv_state.shape:
         raise ValueError("index states must be [B, L, 2 * di] over the same tokens")
     dt = kv_state.dtype
     args = (_ptr(kv_state, dt, "kv_state"), _ptr(score_state, dt, "score_state"), _ptr(gamma, torch.float32, "gamma"),
-            _ptr(cache, dt, "cache"), d, rope_dim, int(overlap), cache.shape[1],
+            _ptr(cache, ct, "cache"), d, rope_dim, int(overlap), cache.shape[1],
             _ptr(idx_kv_state, dt, "idx_kv_state"), _ptr(idx_score_state, dt, "idx_score_state"),
             _ptr(idx_gamma, torch.float32, "idx_gamma"), _ptr(idx_cache, dt, "idx_cache"), di, idx_rope_dim,
-            idx_cache.shape[1], _ptr(pos0, torch.int32, "pos0"), B, L, ratio, eps, rope_base, _dtype_code(kv_state),
-            _stream(stream))
+            idx_cache.shape[1], _ptr(pos0, torch.int32, "pos0"), B, L, ratio, eps, rope_base, code, _stream(stream))
     return _run("csa_compress_kv_index", args, prepare)
 
 
@@ -226,7 +239,7 @@ def csa_compress_index_topk(kv_state, score_state, gamma, cache, idx_kv_state, i
     call (one fused launch plus top-k for decode).  workspace=None calls
     csa_compress_index_topk_noalloc (the library's static scratch)."""
     B, L, md = kv_state.shape
-    d, di = cache.shape[-1], idx_cache.shape[-1]
+    (d, code, ct), di = _cache(cache, kv_state), idx_cache.shape[-1]
     _, S, Hi, qdi = q_idx.shape
     N_cap = idx_cache.shape[1]
     k = topk_idx.shape[-1]
@@ -238,20 +251,16 @@ def csa_compress_index_topk(kv_state, score_state, gamma, cache, idx_kv_state, i
         raise ValueError("q_idx dims must equal the index cache's, and both caches must hold N_cap entries")
     dt = kv_state.dtype
     head = (_ptr(kv_state, dt, "kv_state"), _ptr(score_state, dt, "score_state"), _ptr(gamma, torch.float32, "gamma"),
-            _ptr(cache, dt, "cache"), d, rope_dim, int(overlap), _ptr(idx_kv_state, dt, "idx_kv_state"),
+            _ptr(cache, ct, "cache"), d, rope_dim, int(overlap), _ptr(idx_kv_state, dt, "idx_kv_state"),
             _ptr(idx_score_state, dt, "idx_score_state"), _ptr(idx_gamma, torch.float32, "idx_gamma"),
             _ptr(idx_cache, dt, "idx_cache"), idx_rope_dim, _ptr(state_pos0, torch.int32, "state_pos0"), L,
             _ptr(q_idx, dt, "q_idx"), _ptr(w, torch.float32, "w"), _ptr(q_pos, torch.int32, "q_pos"),
             _ptr(topk_idx, torch.int32, "topk_idx"), _ptr(topk_score, torch.float32, "topk_score"))
-    tail = (B, S, Hi, di, N_cap, k, ratio, 0 if relu else CSA_INDEX_NO_RELU, eps, rope_base, _dtype_code(kv_state),
-            _stream(stream))
+    tail = (B, S, Hi, di, N_cap, k, ratio, 0 if relu else CSA_INDEX_NO_RELU, eps, rope_base, code, _stream(stream))
     if workspace is None:
         return _run("csa_compress_index_topk_noalloc", head + tail, prepare)
     ws_bytes = workspace.numel() * workspace.element_size()
     return _run("csa_compress_index_topk", head + (_ptr(workspace, None, "workspace"), ws_bytes) + tail, prepare)
-
-
-CSA_BF16_KV_FP8 = 2
 
 
 def _kv(q, *rows):

@@ -53,6 +53,20 @@ int check_dtype(const char* fn, int dtype) {
   return CSA_OK;
 }
 
+// Compressor entry points: CSA_BF16_KV_FP8 means bf16 states with the main
+// cache (d = 512, rope_dim = 64) in FP8 rows; the index-key cache stays bf16.
+int check_dtype_cmp(const char* fn, int dtype, int d, int rope_dim) {
+  if (dtype == CSA_BF16_KV_FP8) {
+    if (d != 512 || rope_dim != 64)
+      return fail(CSA_ERR_UNSUPPORTED, "%s: an FP8 cache needs d = 512 and rope_dim = 64", fn);
+    return CSA_OK;
+  }
+  return check_dtype(fn, dtype);
+}
+
+// the element type of states and bf16 caches
+int elem_dtype(int dtype) { return dtype == CSA_BF16_KV_FP8 ? CSA_BF16 : dtype; }
+
 int launched(const char* fn, hipError_t e) {
   if (e != hipSuccess) return fail(CSA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
   return ok();
@@ -115,7 +129,7 @@ int csa_compress(const void* kv_state, const void* score_state, const float* gam
                  int B, int L, int d, int rope_dim, int ratio, int overlap, int N_cap, float eps, float rope_base,
                  int dtype, csa_stream_t stream) {
   const char* fn = "csa_compress";
-  if (int rc = check_dtype(fn, dtype)) return rc;
+  if (int rc = check_dtype_cmp(fn, dtype, d, rope_dim)) return rc;
   REQ_PTR(kv_state);
   REQ_PTR(score_state);
   REQ_PTR(gamma);
@@ -129,8 +143,9 @@ int csa_compress(const void* kv_state, const void* score_state, const float* gam
   REQ(eps >= 0.f, "%s: eps must be >= 0", fn);
   REQ((L + ratio - 1) / ratio + 1 <= 65535 * 1024, "%s: L too large", fn);
   REQ(B <= 65535, "%s: B must be <= 65535", fn);
-  const csa::CompressJob job{kv_state, score_state, gamma, cache, d, rope_dim, overlap, N_cap};
-  return launched(fn, csa_host::launch_compress(&job, 1, pos0, B, L, ratio, eps, rope_base, dtype,
+  const csa::CompressJob job{kv_state, score_state, gamma, cache, d, rope_dim, overlap, N_cap,
+                             dtype == CSA_BF16_KV_FP8};
+  return launched(fn, csa_host::launch_compress(&job, 1, pos0, B, L, ratio, eps, rope_base, elem_dtype(dtype),
                                                 (hipStream_t)stream));
 }
 
@@ -140,7 +155,7 @@ int csa_compress_kv_index(const void* kv_state, const void* score_state, const f
                           int idx_rope_dim, int idx_N_cap, const int32_t* pos0, int B, int L, int ratio, float eps,
                           float rope_base, int dtype, csa_stream_t stream) {
   const char* fn = "csa_compress_kv_index";
-  if (int rc = check_dtype(fn, dtype)) return rc;
+  if (int rc = check_dtype_cmp(fn, dtype, d, rope_dim)) return rc;
   REQ_PTR(kv_state);
   REQ_PTR(score_state);
   REQ_PTR(gamma);
@@ -161,10 +176,11 @@ int csa_compress_kv_index(const void* kv_state, const void* score_state, const f
   REQ(eps >= 0.f, "%s: eps must be >= 0", fn);
   REQ((L + ratio - 1) / ratio + 1 <= 65535 * 1024, "%s: L too large", fn);
   REQ(B <= 65535, "%s: B must be <= 65535", fn);
-  const csa::CompressJob jobs[2] = {{kv_state, score_state, gamma, cache, d, rope_dim, overlap, N_cap},
+  const csa::CompressJob jobs[2] = {{kv_state, score_state, gamma, cache, d, rope_dim, overlap, N_cap,
+                                     dtype == CSA_BF16_KV_FP8},
                                     {idx_kv_state, idx_score_state, idx_gamma, idx_cache, di, idx_rope_dim, 1,
-                                     idx_N_cap}};
-  return launched(fn, csa_host::launch_compress(jobs, 2, pos0, B, L, ratio, eps, rope_base, dtype,
+                                     idx_N_cap, 0}};
+  return launched(fn, csa_host::launch_compress(jobs, 2, pos0, B, L, ratio, eps, rope_base, elem_dtype(dtype),
                                                 (hipStream_t)stream));
 }
 
@@ -301,7 +317,9 @@ int csa_compress_index_topk(const void* kv_state, const void* score_state, const
                             int N_cap, int k, int ratio, unsigned flags, float eps, float rope_base, int dtype,
                             csa_stream_t stream) {
   const char* fn = "csa_compress_index_topk";
-  if (int rc = check_index(fn, q_idx, w, idx_cache, q_pos, B, S, Hi, di, N_cap, ratio, flags, dtype)) return rc;
+  if (int rc = check_dtype_cmp(fn, dtype, d, rope_dim)) return rc;
+  const int dt = elem_dtype(dtype);
+  if (int rc = check_index(fn, q_idx, w, idx_cache, q_pos, B, S, Hi, di, N_cap, ratio, flags, dt)) return rc;
   REQ_PTR(kv_state);
   REQ_PTR(score_state);
   REQ_PTR(gamma);
@@ -327,23 +345,24 @@ int csa_compress_index_topk(const void* kv_state, const void* score_state, const
   if (!workspace || workspace_bytes < need)
     return fail(CSA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed (got %zu)", fn, need, workspace_bytes);
   OPT_PTR(workspace);
-  const csa::CompressJob jobs[2] = {{kv_state, score_state, gamma, cache, d, rope_dim, overlap, N_cap},
-                                    {idx_kv_state, idx_score_state, idx_gamma, idx_cache, di, idx_rope_dim, 1, N_cap}};
+  const csa::CompressJob jobs[2] = {{kv_state, score_state, gamma, cache, d, rope_dim, overlap, N_cap,
+                                     dtype == CSA_BF16_KV_FP8},
+                                    {idx_kv_state, idx_score_state, idx_gamma, idx_cache, di, idx_rope_dim, 1, N_cap, 0}};
   float* scores = (float*)workspace;
   void* tws = (char*)workspace + (((size_t)B * S * N_cap * sizeof(float) + 255) & ~(size_t)255);
   const hipStream_t st = (hipStream_t)stream;
   const int gx = (L + ratio - 1) / ratio + 1;
   const csa::FusedCompress F{jobs[0], jobs[1], state_pos0, L, gx, B, 2 * gx * B, eps, std::log2((double)rope_base)};
-  if (csa_host::fused_compress_ok(F, S, Hi, di, N_cap, ratio, dtype)) {
+  if (csa_host::fused_compress_ok(F, S, Hi, di, N_cap, ratio, dt)) {
     // decode: compressors folded into the indexer (new index entries) and the top-k launch (cache rows)
     hipError_t e = csa_host::launch_index_scores_fused(F, q_idx, w, q_pos, scores, B, S, Hi, N_cap, ratio, flags, st);
     if (e != hipSuccess) return launched(fn, e);
     return launched(fn, csa_host::launch_topk(scores, q_pos, topk_idx, topk_score, tws, B, S, N_cap, k, ratio, st,
                                               &F));
   }
-  hipError_t e = csa_host::launch_compress(jobs, 2, state_pos0, B, L, ratio, eps, rope_base, dtype, st);
+  hipError_t e = csa_host::launch_compress(jobs, 2, state_pos0, B, L, ratio, eps, rope_base, dt, st);
   if (e != hipSuccess) return launched(fn, e);
-  e = csa_host::launch_index_scores(q_idx, w, idx_cache, q_pos, scores, B, S, Hi, di, N_cap, ratio, flags, dtype, st);
+  e = csa_host::launch_index_scores(q_idx, w, idx_cache, q_pos, scores, B, S, Hi, di, N_cap, ratio, flags, dt, st);
   if (e != hipSuccess) return launched(fn, e);
   return launched(fn, csa_host::launch_topk(scores, q_pos, topk_idx, topk_score, tws, B, S, N_cap, k, ratio, st));
 }

@@ -249,6 +249,7 @@ struct CompressJob {
   const float* gamma;
   void* cache;
   int d, rope_dim, overlap, N_cap;
+  int fp8;  // 1: cache rows in the FP8 row format (d == 512, rope_dim == 64)
 };
 
 // Both compressors of a CSA decode step folded into the indexer and top-k

@@ -222,6 +222,36 @@ __device__ __forceinline__ float2 compress_finish(const CompressJob& J, float2 y
   return make_float2(a, bb);
 }
 
+// Store the values of pair p of entry g of sequence b.  FP8 rows (J.fp8): the
+// 32 threads of pairs 32c .. 32c+31 hold block c (64 dims) and sit in one
+// half-wave, so the block maximum is an xor-shuffle reduction over 32 lanes;
+// each thread writes its two codes, the block's first thread the exponent,
+// pairs 224..255 the RoPE dims as bf16, threads 0..56 the zero tail.  The
+// values are decided from the float32 results (the rounding is that of
+// csa_quantize_rows).  Called by every thread of whole waves.
+template <typename T>
+__device__ __forceinline__ void store_entry(const CompressJob& J, int b, long g, int p, float2 v) {
+  if (!J.fp8) {
+    T* dst = (T*)J.cache + ((size_t)b * J.N_cap + g) * J.d;
+    Elt<T>::st(dst, 2 * p, v.x);
+    Elt<T>::st(dst, 2 * p + 1, v.y);
+    return;
+  }
+  uint8_t* row = (uint8_t*)J.cache + ((size_t)b * J.N_cap + g) * FP8_ROW_BYTES;
+  float amax = fmaxf(fabsf(v.x), fabsf(v.y));
+#pragma unroll
+  for (int o = 1; o < 32; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+  if (2 * p < FP8_NQ) {
+    const int k = fp8_block_exp(amax);
+    const uint32_t c = fp8_e4m3_rne(ldexpf(v.x, -k)) | (fp8_e4m3_rne(ldexpf(v.y, -k)) << 8);
+    *(uint16_t*)(row + 2 * p) = (uint16_t)c;
+    if ((p & 31) == 0) row[FP8_SCALE_OFF + (p >> 5)] = (uint8_t)(int8_t)k;
+  } else {
+    *(uint32_t*)(row + FP8_NQ + 4 * (p - FP8_NQ / 2)) = (uint32_t)f2bf(v.x) | ((uint32_t)f2bf(v.y) << 16);
+  }
+  if (p < FP8_ROW_BYTES - FP8_SCALE_OFF - 7) row[FP8_SCALE_OFF + 7 + p] = 0;
+}
+
 // One group of 256 consecutive threads (thread p = threadIdx.x % 256 owns
 // channel pair p, d <= 512) writes entry floor(p0/ratio) + x of sequence b if
 // the compressor writes it; valid == false makes the group a bystander.
@@ -253,9 +283,7 @@ __device__ __forceinline__ void compress_task(const CompressJob& J, const int32_
   const float tot = red4[0] + red4[1] + red4[2] + red4[3];
   if (!active) return;
   const float2 v = compress_finish(J, y, tot, g, ratio, eps, log2_base, p, gm0, gm1);
-  T* dst = (T*)J.cache + ((size_t)b * J.N_cap + g) * J.d;
-  Elt<T>::st(dst, 2 * p, v.x);
-  Elt<T>::st(dst, 2 * p + 1, v.y);
+  store_entry<T>(J, b, g, p, v);
 }
 
 // Wide form for entries with many slots (C128A: 128 tokens): a workgroup of
@@ -327,9 +355,7 @@ __device__ __forceinline__ void compress_task_wide(const CompressJob& J, const i
   if (q != 0 || !active) return;
   const float tot = red4[0] + red4[1] + red4[2] + red4[3];
   const float2 v = compress_finish(J, y, tot, g, ratio, eps, log2_base, p, J.gamma[2 * p], J.gamma[2 * p + 1]);
-  T* dst = (T*)J.cache + ((size_t)b * J.N_cap + g) * J.d;
-  Elt<T>::st(dst, 2 * p, v.x);
-  Elt<T>::st(dst, 2 * p + 1, v.y);
+  store_entry<T>(J, b, g, p, v);
 }
 
 }  // namespace csa

@@ -44,7 +44,9 @@ typedef struct ihipStream_t* csa_stream_t; /* identical to hipStream_t */
 #define CSA_BF16 1
 /* bf16 activations (q, out, compressor states) with window and compressed KV
  * rows in the FP8 row format of csa_quantize_rows (attention and compressor
- * entry points; the index-key cache stays bf16). */
+ * entry points; the index-key cache stays bf16).  Compressors write fresh
+ * main-cache entries quantised from their float32 values (d = 512 and
+ * rope_dim = 64 required, CSA_ERR_UNSUPPORTED otherwise). */
 #define CSA_BF16_KV_FP8 2
 
 #define CSA_OK 0

@@ -126,3 +126,98 @@ def test_swa_on_fp8_rows(orc):
                             topk_idx=np.zeros((B, 1, 0), dtype=np.int32), ratio=1, window=window, rope_dim=64)
     assert_close(to_np(out), ref, TOL["bf16"], "fp8 swa: output")
     assert_close(lse.cpu().numpy(), rlse, 1e-3, "fp8 swa: lse")
+
+
+# ---------------------------------------------------------------- whole path with FP8 caches
+from compressed_sparse_attention_c4a_amd import path as P  # noqa: E402
+from parity import check_topk_sets  # noqa: E402
+from test_gpu_parity import CASES  # noqa: E402
+
+FP8_CASES = ["csa_decode_ragged_bf16", "csa_decode_short_ctx_bf16", "csa_prefill_small_bf16", "hca_decode_small_bf16"]
+
+
+def _fp8_copies(inp, orc):
+    """Device and host copies of a workload with the main cache and the window
+    rows in FP8: quantised by the library and by the oracle, bit-identical."""
+    dev = P.to_device(inp)
+    dev["cmp_cache"] = K.csa_quantize_rows(dev["cmp_cache"])
+    dev["win_kv"] = K.csa_quantize_rows(dev["win_kv"])
+    host = dict(inp)
+    host["cmp_cache"] = orc.quantize_rows_fp8(orc.widen(inp["cmp_cache"]))
+    host["win_kv"] = orc.quantize_rows_fp8(orc.widen(inp["win_kv"]))
+    assert np.array_equal(dev["cmp_cache"].cpu().numpy(), host["cmp_cache"])
+    assert np.array_equal(dev["win_kv"].cpu().numpy(), host["win_kv"])
+    return dev, host
+
+
+def _compare_fp8_entries(gpu_rows, orc_rows, orc_vals, what):
+    """Fresh FP8 entries: the kernels decide on their float32 values and the
+    oracle on the float32 rounding of its fp64 values, so a code may differ
+    where the two straddle a rounding boundary; almost every byte must agree,
+    the RoPE dims within one bf16 step and every value within two E4M3 steps
+    of the oracle's value."""
+    g, o = np.asarray(gpu_rows), np.asarray(orc_rows)
+    assert g.shape == o.shape and g.shape[-1] == 640
+    same = np.mean(g[..., :583] == o[..., :583])
+    print(f"[fp8] {what}: {g.shape[0]} entries, {100 * same:.3f}% of code/exponent bytes identical", flush=True)
+    assert same >= 0.999, f"{what}: only {same:.4%} of the bytes agree"
+    assert np.all(g[..., 583:] == 0)
+    from oracle import oracle as orc
+    gd, od = orc.dequantize_rows_fp8(g), orc.dequantize_rows_fp8(o)
+    k = o[..., 576:583].view(np.int8).astype(np.int64)
+    a = np.abs(np.asarray(orc_vals)[..., :448]).reshape(-1, 7, 64) / np.ldexp(1.0, k.reshape(-1, 7))[..., None]
+    _, E = np.frexp(np.maximum(a, 2.0 ** -6))
+    step = np.ldexp(1.0, k.reshape(-1, 7))[..., None] * np.ldexp(1.0, E - 4)
+    assert np.all(np.abs(gd[..., :448].reshape(-1, 7, 64) - np.asarray(orc_vals)[..., :448].reshape(-1, 7, 64))
+                  <= 2 * step + 1e-30)
+    assert np.max(np.abs(gd[..., 448:] - od[..., 448:]) / np.maximum(np.abs(od[..., 448:]), 1e-30)) <= 2.0 ** -7
+
+
+@pytest.mark.parametrize("name", FP8_CASES)
+def test_path_with_fp8_caches(orc, name):
+    inp = CASES[name]
+    sh = inp["shape"]
+    print(f"[fp8] path {name}", flush=True)
+    dev, host = _fp8_copies(inp, orc)
+    ref = orc.pipeline(host)
+    step = P.Step(dev)
+    out = step.run(dev)
+    torch.cuda.synchronize()
+    gcache = dev["cmp_cache"].cpu().numpy()
+    wr = ref["written"]
+    if wr.any():
+        _compare_fp8_entries(gcache[wr], ref["cmp_cache"][wr], ref["cmp_vals"][wr], f"{name}: compressed rows")
+    assert np.array_equal(gcache[~wr], host["cmp_cache"][~wr])        # untouched rows stay as they were
+    topk = None
+    if sh.indexer:
+        topk = step.topk_idx.cpu().numpy()
+        check_topk_sets(topk, ref["topk_idx"], ref["scores"], ref["nvis"], sh.k)
+    # the oracle's attention over the GPU's own FP8 cache and selection
+    o2, l2, _ = orc.attn(inp["q"], gcache, host["win_kv"], inp["sink"], inp["q_pos"], topk_idx=topk,
+                         ratio=sh.ratio, win_pos0=inp.get("win_pos0"), window=sh.window, rope_dim=sh.rope)
+    assert_close(to_np(out), o2, TOL["bf16"], f"fp8 {name}: output")
+
+
+def test_fused_decode_with_fp8_cache_equals_separate_calls(orc):
+    inp = CASES["csa_decode_ragged_bf16"]
+    sh = inp["shape"]
+    res = []
+    for fused in (False, True):
+        d, _ = _fp8_copies(inp, orc)
+        idx = torch.empty((sh.B, sh.S, sh.k), dtype=torch.int32, device="cuda")
+        ws = torch.empty(K.csa_index_topk_workspace_size(sh.B, sh.S, sh.N_cap, sh.k), dtype=torch.uint8,
+                         device="cuda")
+        if fused:
+            K.csa_compress_index_topk(d["kv_state"], d["score_state"], d["gamma"], d["cmp_cache"], d["idx_kv_state"],
+                                      d["idx_score_state"], d["idx_gamma"], d["idx_cache"], d["state_pos0"],
+                                      d["q_idx"], d["w"], d["q_pos"], idx, ratio=sh.ratio, overlap=sh.overlap,
+                                      rope_dim=sh.rope, idx_rope_dim=sh.idx_rope, workspace=ws)
+        else:
+            K.csa_compress_kv_index(d["kv_state"], d["score_state"], d["gamma"], d["cmp_cache"], d["idx_kv_state"],
+                                    d["idx_score_state"], d["idx_gamma"], d["idx_cache"], d["state_pos0"],
+                                    ratio=sh.ratio, overlap=sh.overlap, rope_dim=sh.rope, idx_rope_dim=sh.idx_rope)
+            K.csa_index_topk(d["q_idx"], d["w"], d["idx_cache"], d["q_pos"], idx, ratio=sh.ratio, workspace=ws)
+        torch.cuda.synchronize()
+        res.append((d["cmp_cache"].cpu().numpy(), d["idx_cache"].cpu().view(torch.int16).numpy(), idx.cpu().numpy()))
+    for a, b in zip(res[0], res[1]):
+        assert np.array_equal(a, b)

@@ -27,14 +27,18 @@ METRIC = "CSA decode queries/s at 32K ctx (B=32, 128 heads); % of MFMA/HBM roofl
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
+# name: (workload generator, KV rows in FP8)
 WORKLOADS = {
-    "csa_decode_32k": "csa_decode_32k",
-    "csa_prefill_8k_at_24k": "csa_prefill_32k",
-    "hca_decode_128k": "hca_decode_128k",
-    "csa_decode_1m": "csa_decode_1m",
-    "hca_decode_32k": "hca_decode_32k",
-    "swa_decode_32k": "swa_decode_32k",
+    "csa_decode_32k": ("csa_decode_32k", False),
+    "csa_prefill_8k_at_24k": ("csa_prefill_32k", False),
+    "hca_decode_128k": ("hca_decode_128k", False),
+    "csa_decode_1m": ("csa_decode_1m", False),
+    "hca_decode_32k": ("hca_decode_32k", False),
+    "swa_decode_32k": ("swa_decode_32k", False),
+    "csa_decode_32k_fp8": ("csa_decode_32k", True),
+    "hca_decode_128k_fp8": ("hca_decode_128k", True),
 }
+FP8_ROW_BYTES = 640
 
 
 def _kernel_sources_hash(files):
@@ -50,14 +54,16 @@ def _kernel_sources_hash(files):
     return h.hexdigest()[:16]
 
 
-def algorithmic(sh):
+def algorithmic(sh, kv_fp8: bool = False):
     """Algorithmic bytes and flops per QUERY of each call: what the method
     must move or compute.  Re-reads and the temporary score buffer are
     excluded: with one position per sequence (decode) every gathered row is a
     distinct read; with a chunk of positions (prefill) each sequence's
     compressed and window rows count once for the whole chunk (consecutive
-    queries share them), q, out, q_idx, w and the index lists once per query."""
+    queries share them), q, out, q_idx, w and the index lists once per query.
+    With FP8 KV rows a compressed or window row is 640 bytes."""
     e = 2 if sh.dtype == "bf16" else 4
+    rb = FP8_ROW_BYTES if kv_fp8 else sh.D * e  # bytes of one compressed / window row
     t_last = sh.q_pos + sh.S - 1
     nvis = min((t_last + 1) // sh.ratio, sh.N_cap)
     nwin = min(sh.window, t_last + 1)
@@ -66,9 +72,9 @@ def algorithmic(sh):
     per = {}
     if sh.swa:  # window rows, q and out only
         win_rows = min(sh.S + sh.window - 1, t_last + 1) if sh.S > 1 else nwin
-        per["attn"] = {"bytes": win_rows / sh.S * sh.D * e + 2 * sh.H * sh.D * e, "flops": 4.0 * sh.H * nwin * sh.D}
+        per["attn"] = {"bytes": win_rows / sh.S * rb + 2 * sh.H * sh.D * e, "flops": 4.0 * sh.H * nwin * sh.D}
         return per, nwin
-    cmp = {"bytes": (2 * sh.state_len * m * sh.D * e + groups * sh.D * e) / sh.S, "flops": 0.0}
+    cmp = {"bytes": (2 * sh.state_len * m * sh.D * e + groups * rb) / sh.S, "flops": 0.0}
     # rows of the window span of the chunk (decode: the window itself)
     win_rows = min(sh.S + sh.window - 1, t_last + 1) if sh.S > 1 else nwin
     if sh.indexer:  # both compressors, the index scores and the top-k in one call
@@ -79,13 +85,13 @@ def algorithmic(sh):
             "flops": 2.0 * sh.Hi * sh.di * nvis_avg}
         reads = nwin + min(sh.k, nvis)
         rows = (win_rows + min(sh.N_cap, nvis if sh.S > 1 else min(sh.k, nvis))) / sh.S if sh.S > 1 else reads
-        per["attn"] = {"bytes": rows * sh.D * e + 2 * sh.H * sh.D * e + sh.k * 4,
+        per["attn"] = {"bytes": rows * rb + 2 * sh.H * sh.D * e + sh.k * 4,
                        "flops": 4.0 * sh.H * reads * sh.D}
     else:
         per["compress"] = cmp
         reads = nwin + nvis
         rows = (win_rows + nvis) / sh.S if sh.S > 1 else reads
-        per["attn"] = {"bytes": rows * sh.D * e + 2 * sh.H * sh.D * e, "flops": 4.0 * sh.H * reads * sh.D}
+        per["attn"] = {"bytes": rows * rb + 2 * sh.H * sh.D * e, "flops": 4.0 * sh.H * reads * sh.D}
     return per, reads
 
 
@@ -129,12 +135,16 @@ def load_traffic(workload: str, kernel_call: str, src_hash: str):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(inp, seconds: float):
+def cpu_baseline(inp, seconds: float, kv_fp8: bool = False):
     """The oracle (as it stands) on the host cores: full passes over the whole
     batch, repeated until about `seconds` of wall time have been spent."""
     from oracle import oracle as O
     from compressed_sparse_attention_c4a_amd import workloads as W
     sh = inp["shape"]
+    if kv_fp8:
+        inp = dict(inp)
+        inp["cmp_cache"] = O.quantize_rows_fp8(O.widen(inp["cmp_cache"]))
+        inp["win_kv"] = O.quantize_rows_fp8(O.widen(inp["win_kv"]))
     O.pipeline(W.slice_batch(inp, 1))           # warm-up (library load, page-in)
     reps, t0 = 0, time.perf_counter()
     while True:
@@ -243,12 +253,17 @@ def main():
     from compressed_sparse_attention_c4a_amd import workloads as W
 
     K.load()
-    sh = getattr(W, WORKLOADS[args.workload])()
+    gen, kv_fp8 = WORKLOADS[args.workload]
+    sh = getattr(W, gen)()
     inp = W.generate(sh)
     dev0 = P.to_device(inp, "cuda")
+    if kv_fp8:  # compressed cache and window rows in FP8 (the library's own quantisation)
+        dev0["cmp_cache"] = K.csa_quantize_rows(dev0["cmp_cache"])
+        dev0["win_kv"] = K.csa_quantize_rows(dev0["win_kv"])
+        torch.cuda.synchronize()
     # rotate enough input copies that the bytes one step touches, summed over
     # the copies, exceed 4x the 256 MB Infinity Cache (bounded by memory)
-    per, reads = algorithmic(sh)
+    per, reads = algorithmic(sh, kv_fp8)
     touched = sum(p["bytes"] for p in per.values()) * sh.B * sh.S
     if sh.indexer:
         touched += 4.0 * sh.B * sh.S * sh.N_cap            # the score buffer
@@ -308,7 +323,7 @@ def main():
     alg_bytes = per[dominant]["bytes"] * Q
     alg_flops = per[dominant]["flops"] * Q
     roof = roofline_of(alg_bytes, alg_flops, dom_ms * 1e-3)
-    roof["traffic"] = load_traffic(sh.name, dominant, src_hash)
+    roof["traffic"] = load_traffic(args.workload, dominant, src_hash)
     roof["kernel"] = dominant
     roof["avg_launch_us"] = round(dom_ms * 1e3, 2)
     roof["algorithmic_bytes_per_launch"] = int(alg_bytes)
@@ -329,13 +344,14 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(inp, args.cpu_seconds)
+        cpu = cpu_baseline(inp, args.cpu_seconds, kv_fp8)
 
     res = {
         "metric": METRIC, "value": round(value, 1), "unit": "queries/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": sh.dtype, "data": "synthetic (seeded N(0,1), PCG64)",
-        "config": {"workload": sh.name, "B": sh.B, "S": sh.S, "context": sh.q_pos + sh.S, "heads": sh.H,
+        "config": {"workload": args.workload, "kv_rows": "fp8 (e4m3, 640 B)" if kv_fp8 else sh.dtype, "B": sh.B,
+                   "S": sh.S, "context": sh.q_pos + sh.S, "heads": sh.H,
                    "head_dim": sh.D, "rope_dim": sh.rope, "ratio": sh.ratio, "entries": sh.N_cap,
                    "topk": sh.k if sh.indexer else None, "window": sh.window,
                    "indexer": f"{sh.Hi}x{sh.di}" if sh.indexer else None, "reads_per_query": reads,

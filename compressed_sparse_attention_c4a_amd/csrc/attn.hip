@@ -256,11 +256,14 @@ __device__ __forceinline__ void store_output(const AttnArgs& a, int qi, int h0, 
   }
 }
 
-// KV8: window and compressed rows in the FP8 row format (common.hpp): the O
-// waves load each row of the next tile into VGPRs (lanes 0..39, 16 bytes each)
-// while the tile in LDS is being used, and after its P.V write the tile
-// dequantised into the same bf16 ring layout (exact), before the barrier that
-// publishes it.  Everything else is the bf16 kernel.
+// KV8: window and compressed rows in the FP8 row format (common.hpp): each
+// 640-byte row goes raw into the top of its LDS row slot with the bf16
+// kernel's direct copies, and the wave that copied it dequantises it in place
+// (exact, one scaled conversion per two values) into the bf16 row layout
+// before the barrier that publishes the tile.  From tile 1 on, the S and the O
+// wave of a row block share its 16 rows (8 each): the S wave between its
+// softmax and the barrier, the O wave between the halves of its P.V.
+// Everything else is the bf16 kernel.
 template <int NHB, bool KV8 = false>
 __global__ __launch_bounds__(512) void attn_tile_kernel(AttnArgs a, int n_hg, int nsplit, int total_items,
                                                         float* __restrict__ part) {
@@ -388,39 +391,50 @@ __global__ __launch_bounds__(512) void attn_tile_kernel(AttnArgs a, int n_hg, in
       dma16_sbase(row, 16u * (uint32_t)lane, ring[ti & 1] + (16 * w4 + rr) * AT_RS);
     }
   };
-  // FP8 rows: the 16 rows this wave copies of tile ti into VGPRs (lane l < 40
-  // holds bytes 16l .. 16l+15 of each row) ...
-  auto load_tile8 = [&](int ti, uint4 (&fr)[16]) {
+  // FP8 rows: the 16 rows this wave copies of tile ti go raw into the top of
+  // their 1088-byte LDS row slots (bytes 448 .. 1087) with the same direct
+  // copies as bf16 rows (lanes 0..39, 640 bytes) ...
+  auto copy_tile8 = [&](int ti, int r0, int nr) {
     int ids[16];
     row_ids(ti, ids);
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
+      if (rr < r0 || rr >= r0 + nr) continue;  // uniform
       const int id = ids[rr];
       const char* row = id >= 0 ? cmpb + (size_t)(uint32_t)id * ROWB : winb + (size_t)(uint32_t)(-1 - id) * ROWB;
-      if (lane < 40) fr[rr] = *(const uint4*)(row + 16 * lane);
+      if (lane < 40) dma16_sbase(row, 16u * (uint32_t)lane, ring[ti & 1] + (16 * w4 + rr) * AT_RS + FP8_NQ);
     }
   };
-  // ... and their bf16 values into stage ti & 1: lane l < 28 writes dims
-  // 16l .. 16l+15 (block l / 4, exponent byte l / 4 of the row, which lane 36
-  // holds), lanes 28..35 the RoPE dims 448 + 8(l - 28) .. +8 unchanged.
-  auto store_tile8 = [&](int ti, const uint4 (&fr)[16]) {
+  // ... and, once landed, are dequantised in place: the codes of dims d sit at
+  // byte 448 + d of the slot and their bf16 values go to byte 2d, so each lane
+  // l < 56 reads its 8 codes (dims 8l .. 8l+7) and the 7 exponents (bytes
+  // 1024 ..) before the wave writes anything; the RoPE dims are bf16 already
+  // and already at bytes 896 .. 1023.  Rows r0 .. r0+nr-1 of the wave's block
+  // (nr a multiple of 8), 8 rows per batch: their reads, one wait, the writes.
+  auto convert_tile8 = [&](int ti, int r0, int nr) {
 #pragma unroll
-    for (int rr = 0; rr < 16; ++rr) {
-      uint8_t* dst = ring[ti & 1] + (16 * w4 + rr) * AT_RS;
-      const uint32_t s0 = (uint32_t)__builtin_amdgcn_readlane((int)fr[rr].x, 36);
-      const uint32_t s1 = (uint32_t)__builtin_amdgcn_readlane((int)fr[rr].y, 36);
-      if (lane < 28) {
-        const int blk = lane >> 2;
-        const int k = (int)(int8_t)(((blk < 4 ? s0 : s1) >> (8 * (blk & 3))) & 0xFFu);
-        const uint4 c = fr[rr];
-        *(uint4*)(dst + 32 * lane) = make_uint4(fp8_pair_to_bf16x2(c.x & 0xFFFFu, k), fp8_pair_to_bf16x2(c.x >> 16, k),
-                                                fp8_pair_to_bf16x2(c.y & 0xFFFFu, k), fp8_pair_to_bf16x2(c.y >> 16, k));
-        *(uint4*)(dst + 32 * lane + 16) = make_uint4(fp8_pair_to_bf16x2(c.z & 0xFFFFu, k),
-                                                     fp8_pair_to_bf16x2(c.z >> 16, k),
-                                                     fp8_pair_to_bf16x2(c.w & 0xFFFFu, k),
-                                                     fp8_pair_to_bf16x2(c.w >> 16, k));
-      } else if (lane < 36) {
-        *(uint4*)(dst + 2 * FP8_NQ + 16 * (lane - 28)) = fr[rr];
+    for (int b0 = 0; b0 < 16; b0 += 8) {
+      if (b0 < r0 || b0 >= r0 + nr) continue;  // uniform
+      uint2 c[8], sk[8];
+#pragma unroll
+      for (int rr = 0; rr < 8; ++rr) {
+        const uint8_t* slot = ring[ti & 1] + (16 * w4 + b0 + rr) * AT_RS;
+        c[rr] = make_uint2(0u, 0u);
+        if (lane < 56) c[rr] = *(const uint2*)(slot + FP8_NQ + 8 * lane);
+        sk[rr] = *(const uint2*)(slot + FP8_NQ + FP8_SCALE_OFF);
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): every read of these rows before any write
+      if (lane < 56) {
+        const int blk = lane >> 3;
+#pragma unroll
+        for (int rr = 0; rr < 8; ++rr) {
+          uint8_t* slot = ring[ti & 1] + (16 * w4 + b0 + rr) * AT_RS;
+          const int k = (int)(int8_t)(((blk < 4 ? sk[rr].x : sk[rr].y) >> (8 * (blk & 3))) & 0xFFu);
+          *(uint4*)(slot + 16 * lane) = make_uint4(fp8_pair_to_bf16x2(c[rr].x & 0xFFFFu, k),
+                                                   fp8_pair_to_bf16x2(c[rr].x >> 16, k),
+                                                   fp8_pair_to_bf16x2(c[rr].y & 0xFFFFu, k),
+                                                   fp8_pair_to_bf16x2(c[rr].y >> 16, k));
+        }
       }
     }
   };
@@ -455,6 +469,11 @@ __global__ __launch_bounds__(512) void attn_tile_kernel(AttnArgs a, int n_hg, in
     }
     lds_barrier();              // X_0 (every wave has its q fragments before tile 1 is copied)
     for (int i = 0; i < ntiles; ++i) {
+      if constexpr (KV8) {
+        // FP8 rows: this S wave copies (and later dequantises) rows 8..15 of
+        // its block of tile i+1, into the stage tile i-1 used
+        if (i + 1 < ntiles) copy_tile8(i + 1, 8, 8);
+      }
       const uint8_t* myrow = ring[i & 1] + (16 * w4 + n) * AT_RS + 16 * g;
       // 1. logits of this wave's 16 rows for the HG heads (two chains per head block)
       f32x4_t S0[NHB], S1[NHB];
@@ -532,6 +551,12 @@ __global__ __launch_bounds__(512) void attn_tile_kernel(AttnArgs a, int n_hg, in
       }
 #pragma unroll
       for (int hb = 0; hb < NHB; ++hb) l_run[hb] += (pv[hb][0] + pv[hb][1]) + (pv[hb][2] + pv[hb][3]);
+      if constexpr (KV8) {
+        if (i + 1 < ntiles) {
+          WAIT_VMCNT(0);  // this wave's copies of tile i+1 have landed
+          convert_tile8(i + 1, 8, 8);
+        }
+      }
       if (i + 1 < ntiles) lds_barrier();  // X_i+1
     }
     // sums over the lane groups, and the running max, for the O waves
@@ -549,7 +574,7 @@ __global__ __launch_bounds__(512) void attn_tile_kernel(AttnArgs a, int n_hg, in
     // transposed reads: rows 32c + 8g + (n >> 2) (+4), dims d0 + 16dt + 4(n & 3)
     const int tr_off = (8 * g + (n >> 2)) * AT_RS + 2 * d0 + 8 * (n & 3);
     // Y_i (and Y'_i on a rescale), then this tile's P.V into o
-    auto pv_tile = [&](int i) {
+    auto pv_tile = [&](int i, auto&& mid) {
       const uint8_t* tile = ring[i & 1];
       lds_barrier();  // Y_i
       if (fbuf[0] | fbuf[1] | fbuf[2] | fbuf[3]) {
@@ -564,6 +589,7 @@ __global__ __launch_bounds__(512) void attn_tile_kernel(AttnArgs a, int n_hg, in
       // O^T[128 dims x HG heads] += R^T[128 x 64 rows] P^T[64 rows x HG heads]
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
+        if (c == 1) mid();  // work that overlaps the first half's matrix ops
         bf16x8_t pf[NHB];
 #pragma unroll
         for (int hb = 0; hb < NHB; ++hb) pf[hb] = *(const bf16x8_t*)&pbuf[16 * hb + n][32 * c + 8 * g];
@@ -584,29 +610,33 @@ __global__ __launch_bounds__(512) void attn_tile_kernel(AttnArgs a, int n_hg, in
       }
     };
     if constexpr (KV8) {
-      // Every iteration of the loop loads the next tile's rows and consumes them,
-      // so no load is pending at the back edge (the compiler would otherwise
-      // wait for all loads before each new one); the last tile is peeled.
-      uint4 fr[16];
+      // the bf16 schedule, with each tile dequantised in place after its
+      // copies land, between the two halves of the previous tile's P.V (so
+      // the conversion overlaps its matrix ops), before the barrier that
+      // publishes it
       if (ntiles > 0) {
-        load_tile8(0, fr);
-        store_tile8(0, fr);
+        copy_tile8(0, 0, 16);
+        WAIT_VMCNT(0);
+        convert_tile8(0, 0, 16);
       }
       lds_barrier();  // X_0
-      for (int i = 0; i + 1 < ntiles; ++i) {
-        load_tile8(i + 1, fr);   // into VGPRs
-        pv_tile(i);
-        store_tile8(i + 1, fr);  // stage (i+1) & 1: tile i-1's, free since X_i
-        lds_barrier();           // X_i+1
+      for (int i = 0; i < ntiles; ++i) {
+        if (i + 1 < ntiles) copy_tile8(i + 1, 0, 8);  // rows 0..7 of the block; the S wave takes 8..15
+        pv_tile(i, [&] {
+          if (i + 1 < ntiles) {
+            WAIT_VMCNT(0);  // this wave's copies of tile i+1 have landed
+            convert_tile8(i + 1, 0, 8);
+          }
+        });
+        if (i + 1 < ntiles) lds_barrier();  // X_i+1
       }
-      if (ntiles > 0) pv_tile(ntiles - 1);
     } else {
       if (ntiles > 0) copy_tile(0);
       WAIT_VMCNT(0);
       lds_barrier();  // X_0
       for (int i = 0; i < ntiles; ++i) {
         if (i + 1 < ntiles) copy_tile(i + 1);  // into the stage tile i-1 used
-        pv_tile(i);
+        pv_tile(i, [] {});
         if (i + 1 < ntiles) {
           WAIT_VMCNT(0);  // this wave's copies of tile i+1 have landed
           lds_barrier();  // X_i+1

@@ -195,12 +195,13 @@ __device__ __forceinline__ uint32_t fp8_e4m3_rne(float v) {
   return sign | ((uint32_t)(e + 7) << 3) | (uint32_t)mant;
 }
 
-// bf16 bits of E4M3 code c times 2^k: exact (the value has at most 4
-// significant bits), so the upper half of the fp32 value is the bf16 value.
+// bf16 pair of the E4M3 codes in bits [0, 16) times 2^k (k in [-120, 120]):
+// exact (a value has at most 4 significant bits), one scaled conversion.
+typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t fp8_pair_to_bf16x2(uint32_t two_codes, int k) {
-  const auto f = __builtin_amdgcn_cvt_pk_f32_fp8((int)two_codes, false);  // codes in bits [0, 16)
-  const uint32_t lo = __float_as_uint(ldexpf(f[0], k)) >> 16, hi = __float_as_uint(ldexpf(f[1], k)) >> 16;
-  return lo | (hi << 16);
+  const float scale = __uint_as_float((uint32_t)(k + 127) << 23);  // 2^k
+  const bf16x2v_t r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)two_codes, scale, false);
+  return __builtin_bit_cast(uint32_t, r);
 }
 
 // Inclusive prefix sum over the 64 lanes of a wave with DPP moves (no LDS

@@ -35,6 +35,22 @@ def test_dequantize_every_code_and_exponent(orc):
     assert np.array_equal((got[~nan].astype(np.uint32) << 16).view(np.float32).astype(np.float64), ref[~nan])
 
 
+def test_dequantize_all_codes_at_every_exponent(orc):
+    """Each exponent k in [-120, 120] with every code in every block (4 rows
+    per k), against the oracle's exact values: the extremes give bf16
+    subnormals (2^-129) and 448 * 2^120."""
+    ks = np.arange(-120, 121)
+    codes = np.concatenate([np.arange(256, dtype=np.uint8)] * 7)          # 1792 = 4 rows x 448
+    rows = np.zeros((len(ks) * 4, 640), dtype=np.uint8)
+    rows[:, :448] = np.tile(codes.reshape(4, 448), (len(ks), 1))
+    rows[:, 576:583] = np.repeat(ks, 4)[:, None].astype(np.int8).view(np.uint8)
+    got = _bits(K.csa_dequantize_rows(torch.from_numpy(rows).cuda()))
+    ref = orc.dequantize_rows_fp8(rows)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan((got.astype(np.uint32) << 16).view(np.float32)), nan)
+    assert np.array_equal(got[~nan], orc.round_bf16(ref[~nan]))
+
+
 def _hard_rows(rng, R):
     x = rng.standard_normal((R, 512)).astype(np.float32)
     scale = np.exp2(rng.integers(-30, 20, size=(R, 8))).astype(np.float32)

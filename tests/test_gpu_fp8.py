@@ -237,3 +237,30 @@ def test_fused_decode_with_fp8_cache_equals_separate_calls(orc):
         res.append((d["cmp_cache"].cpu().numpy(), d["idx_cache"].cpu().view(torch.int16).numpy(), idx.cpu().numpy()))
     for a, b in zip(res[0], res[1]):
         assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("name", ["csa_decode_32k", "hca_decode_128k"])
+def test_full_size_decode_with_fp8_caches(orc, name):
+    """The bench's FP8 workloads (the same Step and launch shapes): fresh
+    entries, the index sets, and every output against the oracle on the
+    GPU's own FP8 cache and selection."""
+    sh = getattr(W, name)()
+    inp = W.generate(sh)
+    print(f"[fp8] full size {name}", flush=True)
+    dev, host = _fp8_copies(inp, orc)
+    step = P.Step(dev)
+    out = step.run(dev)
+    torch.cuda.synchronize()
+    ref = orc.pipeline(host)
+    wr = ref["written"]
+    assert wr.any()
+    gcache = dev["cmp_cache"].cpu().numpy()
+    _compare_fp8_entries(gcache[wr], ref["cmp_cache"][wr], ref["cmp_vals"][wr], f"{name}: compressed rows")
+    topk = None
+    if sh.indexer:
+        topk = step.topk_idx.cpu().numpy()
+        check_topk_sets(topk, ref["topk_idx"], ref["scores"], ref["nvis"], sh.k)
+    o2, l2, _ = orc.attn(inp["q"], gcache, host["win_kv"], inp["sink"], inp["q_pos"], topk_idx=topk,
+                         ratio=sh.ratio, window=sh.window, rope_dim=sh.rope)
+    assert_close(to_np(out), o2, TOL["bf16"], f"fp8 {name}: output")
+    assert_close(step.lse.cpu().numpy(), l2, 1e-3, f"fp8 {name}: lse")

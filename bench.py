@@ -232,6 +232,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="wall time of the CPU oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-projections", action="store_true", help="skip the Q/O projection measurement")
+    ap.add_argument("--graph", action="store_true",
+                    help="time the steps as replays of one captured HIP graph per input copy (path.GraphStep)")
     ap.add_argument("--projections-only", action="store_true",
                     help="only measure the Q/O projections at decode (B=32) and print their JSON")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -279,12 +281,16 @@ def main():
 
     calls = list(per)
     Q = sh.B * sh.S
+    graphs = [P.GraphStep(d, st) for d, st in zip(devs, steps)] if args.graph else None
 
     def run_one(i, events=None):
         d, st, pc = devs[i % R], steps[i % R], prepared[i % R]
         if events is None:
-            for _, fn in pc:
-                fn()
+            if graphs is not None:
+                graphs[i % R].run()
+            else:
+                for _, fn in pc:
+                    fn()
         else:
             st.run_timed(d, stream, events, pc)
 
@@ -305,11 +311,12 @@ def main():
     # events on every EVERY-th step only: an event record costs the stream a
     # few microseconds, so bracketing every step would inflate the step time.
     EVERY = 8
-    dom_events = {dominant: []}
+    dom_events = {dominant: []} if graphs is None else {dominant: list(ev_probe[dominant])}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        run_one(args.warmup + n_probe + i, dom_events if i % EVERY == 0 else None)
+        # (graph replays are not bracketed: the dominant call's time is the probe's)
+        run_one(args.warmup + n_probe + i, dom_events if (i % EVERY == 0 and graphs is None) else None)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     dom_ms = float(np.mean([a.elapsed_time(b) for a, b in dom_events[dominant]]))
@@ -359,6 +366,7 @@ def main():
         "roofline": roof,
         "whole_step": whole,
         "call_us": {c: round(v * 1e3, 2) for c, v in avg_probe.items()},
+        "launch": "hip graph replay per step" if graphs is not None else "eager library calls",
         # the projections around the same layer (not part of `value`): the
         # decode step of a whole attention block adds their time
         "projections": proj,

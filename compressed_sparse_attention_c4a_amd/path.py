@@ -130,3 +130,32 @@ class LayerStack:
         for _, fn in self.calls(stream):
             fn()
         return [st.out for st in self.steps]
+
+
+class GraphStep:
+    """One pass of the path captured once into a HIP graph and replayed: the
+    same library launches (the Prepared calls of Step, on the capture stream),
+    issued by one graph launch instead of one host call each.  Nothing is
+    allocated during capture (outputs and workspaces belong to the Step) and
+    no launch path of the library records a memset.  Replays overwrite the
+    Step's outputs in place."""
+
+    def __init__(self, dev: dict, step: "Step" = None):
+        self.dev = dev
+        self.step = step if step is not None else Step(dev)
+        self.step.run(dev)  # first calls outside the capture (library load, one-time host work)
+        torch.cuda.synchronize()
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            cs = torch.cuda.current_stream()
+            for _, fn in self.step.calls(dev, cs, prepare=True):
+                fn()
+        torch.cuda.synchronize()
+
+    @property
+    def out(self):
+        return self.step.out
+
+    def run(self):
+        self.graph.replay()
+        return self.step.out

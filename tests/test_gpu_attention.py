@@ -153,3 +153,32 @@ def test_window_only_layer(orc, H, q_pos):
                             topk_idx=np.zeros((B, S, 0), dtype=np.int32), window=128, rope_dim=64)
     assert_close(to_np(out), ref, TOL["bf16"], "window only: output")
     assert_close(lse.cpu().numpy(), rlse, 1e-3, "window only: lse")
+
+
+@pytest.mark.parametrize("sink_inf", [False, True])
+@pytest.mark.parametrize("dense", [False, True])
+def test_moving_maximum_and_short_contexts_32_heads(orc, dense, sink_inf):
+    """32 heads per workgroup in 4 candidate splits with logits of a wide
+    spread (softmax scale 1, standard deviation about 22): the running maximum
+    leaves its headroom in many tiles, so the rescale of P and of the
+    accumulated output is taken again and again; with a -inf sink it is taken
+    on the first valid logit.  Contexts from 1 to 4800 positions leave dense
+    splits with no tile and tiles with a ragged tail."""
+    B, S, H, N_cap, W_cap, k = 16, 1, 128, 1200, 128, 512
+    q_pos = [0, 1, 2, 30, 31, 32, 63, 64, 95, 127, 128, 200, 700, 2047, 4000, 4799]
+    x = _inputs(23 + dense, B, S, H, N_cap, W_cap, k, q_pos)
+    sink = np.full((H,), -np.inf, dtype=np.float32) if sink_inf else x["sink"] * np.float32(8.0)
+    out = torch.empty((B, S, H, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, S, H), dtype=torch.float32, device="cuda")
+    print(f"[attn] moving max dense={dense} sink_inf={sink_inf}", flush=True)
+    if dense:
+        K.hca_attn(_dev(x["q"]), _dev(x["cmp"]), _dev(x["win"]), None, _dev(sink), _dev(x["q_pos"]), out, lse,
+                   ratio=4, rope_dim=64, window=128, softmax_scale=1.0)
+    else:
+        K.csa_sparse_attn(_dev(x["q"]), _dev(x["cmp"]), _dev(x["topk"]), _dev(x["win"]), None, _dev(sink),
+                          _dev(x["q_pos"]), out, lse, rope_dim=64, window=128, softmax_scale=1.0)
+    ref, rlse, _ = orc.attn(x["q"], x["cmp"], x["win"], sink, x["q_pos"], topk_idx=None if dense else x["topk"],
+                            ratio=4, window=128, rope_dim=64, scale=1.0)
+    torch.cuda.synchronize()
+    assert_close(to_np(out), ref, TOL["bf16"], f"moving max dense={dense} sink_inf={sink_inf}: output")
+    assert_close(lse.cpu().numpy(), rlse, 1e-3, f"moving max dense={dense} sink_inf={sink_inf}: lse")

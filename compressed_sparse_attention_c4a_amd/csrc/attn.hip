@@ -796,16 +796,31 @@ static AttnPlan attn_plan_nhb(long Q, int H, int n_cand, int nhb) {
   return p;
 }
 
+// Predicted time of a plan: one workgroup per CU (the LDS ring takes ~158
+// KiB), so ceil(workgroups / 256) rounds, each a set-up plus the tiles of one
+// split, and the merge when the list is split.  The constants were measured on
+// MI355X at decode shapes (16 and 32 heads per workgroup over 3-18 tiles per
+// split, with and without splits): set-up 4.3 / 6.2 us, a 64-row tile 1.37 /
+// 1.75 us, the merge 4.7 us.
+static double attn_plan_cost(const AttnPlan& p, int n_cand) {
+  const int nt = (n_cand + AT_TR - 1) / AT_TR;
+  const int tps = (nt + p.nsplit - 1) / p.nsplit;
+  const long rounds = (p.total + 255) / 256;
+  const double setup = p.nhb == 2 ? 6.2 : 4.3, tile = p.nhb == 2 ? 1.75 : 1.37;
+  return (double)rounds * (setup + tps * tile) + (p.nsplit > 1 ? 4.7 : 0.0);
+}
+
 // 32 heads per workgroup (each gathered row serves twice the heads per LDS
-// pass), unless that needs more than 4 candidate splits: then 16 heads, so
-// the chip fills with half the splits and the merge reads half the partials
-// (csa_decode_1m, 8 queries: 23.4 -> 19.5 us per call).
+// pass) or 16 (twice the workgroups, a cheaper set-up and tile), whichever the
+// cost model predicts faster: 32 heads for many queries (fewer rounds of
+// workgroups) and for long lists split twice (csa_decode_32k), 16 heads for
+// short lists at decode (hca_decode_32k, window-only layers: no split, no
+// merge) and for few queries (csa_decode_1m: 8 queries, 4 splits instead of 8).
 static AttnPlan attn_plan(long Q, int H, int n_cand) {
-  if (H % 32 == 0) {
-    const AttnPlan p2 = attn_plan_nhb(Q, H, n_cand, 2);
-    if (p2.nsplit <= 4) return p2;
-  }
-  return attn_plan_nhb(Q, H, n_cand, 1);
+  const AttnPlan p1 = attn_plan_nhb(Q, H, n_cand, 1);
+  if (H % 32 != 0) return p1;
+  const AttnPlan p2 = attn_plan_nhb(Q, H, n_cand, 2);
+  return attn_plan_cost(p2, n_cand) <= attn_plan_cost(p1, n_cand) ? p2 : p1;
 }
 
 size_t attn_workspace_size(int B, int S, int H, int D, int n_cand) {

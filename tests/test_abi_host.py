@@ -49,6 +49,24 @@ def test_compress_validation(lib):
     assert _compress(lib, B=0) == CSA_ERR_SHAPE
 
 
+def test_attention_plan(lib):
+    """Head grouping and splits come from the cost model; read back through the
+    workspace size (one 33024-byte partial per workgroup when the list is
+    split, none otherwise)."""
+    part = 4 * 8 * 2 * 64 * 4 * 2 + 64 * 4
+
+    def ws(B, H, n_cand):
+        return lib.csa_attn_workspace_size(B, 1, H, 512, n_cand)
+
+    assert ws(32, 128, 1152) == 256 * part   # CSA decode, 32K: 32 heads, 2 splits (16 heads: no split)
+    assert ws(64, 128, 1152) == 0            # HCA decode, 128K: 32 heads, no split
+    assert ws(32, 128, 384) == 0             # HCA decode, 32K: 16 heads, no split (32 heads: 2 splits)
+    assert ws(32, 128, 128) == 0             # window-only layer: 16 heads, no split
+    assert ws(8192, 128, 1152) == 0          # prefill chunk
+    assert ws(5, 128, 224) == 80 * part      # 5 queries: 16 heads (8 groups) x 2 splits
+    assert ws(16, 128, 1152) == 256 * part   # 16 queries: 32 heads x 4 splits
+
+
 def test_index_and_topk_validation(lib):
     a = (P, P, P, P, P)
     assert lib.csa_index_scores(None, P, P, P, P, 1, 1, 64, 128, 100, 4, 0, 1, None) == CSA_ERR_NULL

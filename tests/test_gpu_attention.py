@@ -48,11 +48,11 @@ def _dev(a):
 
 VARIANTS = {
     # name: (B, S, H, N_cap, W_cap, k, q_pos, linear window, window)
-    # 32 heads per workgroup, 2 splits (sparse) / 16 heads, 6 splits, most of them empty (dense:
-    # 32 heads would need more than 4 splits)
+    # (the plan, 16 or 32 heads per workgroup and the splits, is the cost model's choice)
+    # 16 heads per workgroup, 2 splits (sparse) / 6 splits, most of them empty (dense)
     "split_decode_short_ctx": (5, 1, 128, 600, 128, 96, [2399, 1000, 130, 7, 0], False, 128),
-    # 32 heads per workgroup at the split limit: 64 items, 4 splits
-    "h128_four_splits": (16, 1, 128, 2000, 128, 512, list(range(7999, 7999 - 16 * 37, -37)), False, 128),
+    # 32 heads per workgroup, 64 items, 4 splits
+    "h128_four_splits": (16, 1, 128, 2000, 128, 1024, list(range(7999, 7999 - 16 * 37, -37)), False, 128),
     # 256 (query, head group) items: no split
     "nosplit_decode": (64, 1, 128, 300, 128, 40, list(range(400, 1040, 10)), False, 128),
     "prefill_linear_window": (1, 160, 128, 200, 160 + 127, 48, [600], True, 128),
@@ -164,7 +164,7 @@ def test_moving_maximum_and_short_contexts_32_heads(orc, dense, sink_inf):
     accumulated output is taken again and again; with a -inf sink it is taken
     on the first valid logit.  Contexts from 1 to 4800 positions leave dense
     splits with no tile and tiles with a ragged tail."""
-    B, S, H, N_cap, W_cap, k = 16, 1, 128, 1200, 128, 512
+    B, S, H, N_cap, W_cap, k = 16, 1, 128, 1200, 128, 1024
     q_pos = [0, 1, 2, 30, 31, 32, 63, 64, 95, 127, 128, 200, 700, 2047, 4000, 4799]
     x = _inputs(23 + dense, B, S, H, N_cap, W_cap, k, q_pos)
     sink = np.full((H,), -np.inf, dtype=np.float32) if sink_inf else x["sink"] * np.float32(8.0)

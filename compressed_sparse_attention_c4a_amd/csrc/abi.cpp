@@ -351,7 +351,7 @@ int csa_compress_index_topk(const void* kv_state, const void* score_state, const
   float* scores = (float*)workspace;
   void* tws = (char*)workspace + (((size_t)B * S * N_cap * sizeof(float) + 255) & ~(size_t)255);
   const hipStream_t st = (hipStream_t)stream;
-  const int gx = (L + ratio - 1) / ratio + 1;
+  const int gx = csa_host::compress_gx(L, ratio);
   const csa::FusedCompress F{jobs[0], jobs[1], state_pos0, L, gx, B, 2 * gx * B, eps, std::log2((double)rope_base)};
   if (csa_host::fused_compress_ok(F, S, Hi, di, N_cap, ratio, dt)) {
     // decode: compressors folded into the indexer (new index entries) and the top-k launch (cache rows)

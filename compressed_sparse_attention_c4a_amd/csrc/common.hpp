@@ -267,6 +267,11 @@ struct FusedCompress {
 
 // Host-side launch helpers implemented per kernel file; called from abi.cpp.
 namespace csa_host {
+// Groups g = floor(p0 / ratio) + x that can be complete inside a buffer of L
+// tokens starting at p0: with p0 = a*ratio + b and L = c*ratio + e (0 <= b, e
+// < ratio) the last complete group is floor((p0 + L) / ratio) - 1, so x <=
+// c + floor((b + e) / ratio) - 1 <= ceil(L / ratio) - 1.
+inline int compress_gx(int L, int ratio) { return (L + ratio - 1) / ratio; }
 hipError_t launch_compress(const csa::CompressJob* jobs, int njobs, const int32_t* pos0, int B, int L, int ratio,
                            float eps, float base, int dtype, hipStream_t st);
 hipError_t launch_index_scores(const void* q, const float* w, const void* K, const int32_t* q_pos, float* scores,

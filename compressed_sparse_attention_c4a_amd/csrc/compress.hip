@@ -35,8 +35,8 @@ using namespace csa;
 
 hipError_t launch_compress(const CompressJob* jobs, int njobs, const int32_t* pos0, int B, int L, int ratio,
                            float eps, float base, int dtype, hipStream_t st) {
-  // Groups that can intersect [pos0, pos0 + L): at most ceil(L / ratio) + 1.
-  dim3 grid((unsigned)((L + ratio - 1) / ratio + 1), (unsigned)B, (unsigned)njobs);
+  // Candidate groups per sequence: compress_gx (a complete group lies inside the buffer).
+  dim3 grid((unsigned)compress_gx(L, ratio), (unsigned)B, (unsigned)njobs);
   const CompressJob j1 = njobs > 1 ? jobs[1] : jobs[0];
   const double l2b = std::log2((double)base);
   const int nslot = std::max(jobs[0].overlap ? 2 * ratio : ratio, j1.overlap ? 2 * ratio : ratio);

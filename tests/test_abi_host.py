@@ -201,3 +201,19 @@ def test_fp8_attention_shapes(lib):
     assert _attn(lib, dtype=2, D=256, rope=64) == CSA_ERR_UNSUPPORTED
     assert _attn(lib, dtype=2, k=4096) == CSA_ERR_UNSUPPORTED
     assert _attn(lib, dtype=3) == CSA_ERR_DTYPE
+
+
+def test_compressor_grid_covers_every_complete_group():
+    """The compressor launches ceil(L / ratio) candidate groups per sequence
+    (x = 0 .. ceil(L / ratio) - 1 after floor(p0 / ratio)): brute force over
+    buffer starts (negative ones too), lengths and ratios finds no complete
+    group beyond that."""
+    for ratio in (1, 3, 4, 7, 128):
+        for L in range(1, 3 * ratio + 5):
+            gx = (L + ratio - 1) // ratio
+            for p0 in range(-2 * ratio - 3, 3 * ratio + 3):
+                g0 = p0 // ratio
+                for g in range(g0 - 1, g0 + gx + 3):
+                    complete = g * ratio >= p0 and g * ratio + ratio - 1 <= p0 + L - 1
+                    if complete:
+                        assert 0 <= g - g0 < gx, (ratio, L, p0, g)

@@ -158,10 +158,11 @@ __global__ __launch_bounds__(64) void attn_generic_kernel(AttnArgs a) {
 // (split 0).
 //
 // Splits: when there are too few (query, head group) items to fill the chip,
-// an item's tiles are divided between NS workgroups (16 heads per workgroup
-// when 32 would need more than 4), each of which writes its O divided by its
-// own sum (bf16), its running max and its sum (fp32) to the workspace;
-// attn_merge_kernel (launched next on the same stream) combines them.
+// an item's tiles are divided between NS workgroups (16 or 32 heads per
+// workgroup as the plan's cost model picks), each of which writes its O
+// divided by its own sum (bf16), its running max and its sum (fp32) to the
+// workspace; attn_merge_kernel (launched next on the same stream) combines
+// them.
 // LDS rows are 1088 bytes apart (64 bytes of padding, no permutation): the
 // row reads of QK^T (ds_read_b128) and the transposed reads of P.V
 // (ds_read_b64_tr_b16) then run at 113-117 B/clk/CU on gfx950, against 95-101

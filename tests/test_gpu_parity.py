@@ -243,3 +243,45 @@ def test_repeat_runs_are_bitwise_identical(case):
     a = raw_np(step.run(dev)).copy()
     b = raw_np(step.run(dev))
     np.testing.assert_array_equal(a, b)
+
+
+def _random_decode_cases(n=8, seed=77):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        B = int(rng.integers(1, 13))
+        N_cap = int(rng.choice([64, 700, 3000, 8192, 9000]))
+        k = int(rng.choice([16, 256, 1024, 2048]))
+        state_len = 8 if rng.integers(0, 4) else int(rng.integers(4, 8))   # 2 * ratio tokens, sometimes fewer
+        q_pos = rng.integers(0, 4 * N_cap + 64, B)
+        q_pos[rng.integers(0, B)] = 4 * int(rng.integers(0, N_cap)) + 3   # one sequence completes an entry
+        q_pos = np.maximum(q_pos, state_len - 1)    # the state starts at position 0 or later
+        out.append((f"d{i}", B, N_cap, k, state_len, q_pos.astype(np.int32), 900 + i))
+    return out
+
+
+@pytest.mark.parametrize("case", _random_decode_cases(), ids=lambda c: c[0])
+def test_fused_decode_random_positions(orc, case):
+    """Seeded random decode batches (ragged positions, states of 8 tokens (at
+    times 4 to 7) ending at each query's position, caches of 64 to 9000 entries, k of 16
+    to 2048): the fused call equals the separate calls bit for bit, and the
+    cache rows it writes and its top-k sets match the oracle."""
+    name, B, N_cap, k, L, q_pos, seed = case
+    print(f"[fused-random] {name}: B={B} N_cap={N_cap} k={k} L={L} q_pos={q_pos.tolist()}", flush=True)
+    sh = W.Shape(name=f"fused_random_{name}", B=B, S=1, N_cap=N_cap, window=128, W_cap=128, state_len=L, k=k,
+                 seed=seed)
+    inp = dict(W.generate(sh))
+    inp["q_pos"] = q_pos
+    inp["state_pos0"] = (q_pos - (L - 1)).astype(np.int32)
+    _assert_fused_equal(inp)
+    ref = orc.pipeline(inp)
+    (d, idx, _), _ = _separate_and_fused(inp)
+    wr = ref["written"]
+    if wr.any():
+        assert_close(to_np(d["cmp_cache"])[wr], ref["cmp_vals"][wr], TOL["bf16"], f"{name}: compressed rows")
+    iw = ref["idx_written"]
+    if iw.any():
+        assert_close(to_np(d["idx_cache"])[iw], ref["idx_vals"][iw], TOL["bf16"], f"{name}: index rows")
+    nvis = np.minimum((q_pos + 1) // 4, N_cap)
+    check_topk_sets(idx.cpu().numpy().reshape(B, k), ref["topk_idx"].reshape(B, k), ref["scores"].reshape(B, -1),
+                    nvis, k)

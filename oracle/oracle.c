@@ -331,8 +331,9 @@ void orc_topk(const double* scores, const int32_t* nvis, int B, int S, int N_cap
  * Candidates of query position t:
  *   window rows of positions u in [max(0, t-window+1), t]; with win_pos0 ==
  *   NULL the window buffer is a ring (row u mod W_cap), else row u-win_pos0[b];
- *   compressed entries: if topk_idx != NULL, the non-negative entries of
- *   topk_idx[b,s,:k]; otherwise (dense, HCA) every s < (t+1)/ratio.
+ *   compressed entries: if topk_idx != NULL, the entries of topk_idx[b,s,:k]
+ *   in [0, N_cap) (padding -1 and indices past the cache select nothing);
+ *   otherwise (dense, HCA) every s < (t+1)/ratio.
  * logits l = scale * <q_h, row>;  Z = sum exp(l) + exp(sink_h);
  * o_h = sum exp(l)/Z * row; out = o with its last rope_dim dims rotated by
  * -theta(t).  lse[b,s,h] = log Z (nullable).  ncand[b,s] = candidate count
@@ -355,8 +356,10 @@ int orc_attn(const void* q, int qdt, const void* cmp_cache, int cdt, const int32
       long nv = (t + 1) / (ratio > 0 ? ratio : 1);
       if (nv > N_cap) nv = N_cap;
       if (topk_idx) {
+        /* a list entry that names no cache row (< 0: padding; >= N_cap)
+         * selects nothing */
         for (int j = 0; j < k; ++j)
-          if (topk_idx[qi * k + j] >= 0) ++ncmp;
+          if (topk_idx[qi * k + j] >= 0 && topk_idx[qi * k + j] < N_cap) ++ncmp;
       } else {
         ncmp = nv;
       }
@@ -376,7 +379,7 @@ int orc_attn(const void* q, int qdt, const void* cmp_cache, int cdt, const int32
       if (topk_idx) {
         for (int i = 0; i < k; ++i) {
           int e = topk_idx[qi * k + i];
-          if (e < 0) continue;
+          if (e < 0 || e >= N_cap) continue;
           for (int c = 0; c < D; ++c) rows[j][c] = ld(cmp_cache, cdt, ((size_t)b * N_cap + e) * D + c);
           ++j;
         }

@@ -420,3 +420,23 @@ def test_queries_never_see_the_future(orc):
     got = orc.pipeline(pert)
     np.testing.assert_array_equal(got["out"][:, :t0 + 1], base["out"][:, :t0 + 1])
     np.testing.assert_array_equal(got["topk_idx"][:, :t0 + 1], base["topk_idx"][:, :t0 + 1])
+
+
+def test_attention_list_entries_past_the_cache_select_nothing(orc):
+    """A top-k list entry that names no cache row (-1 padding, or an index at
+    or past N_cap) selects nothing: the result equals the list with those
+    entries removed."""
+    rng = np.random.default_rng(31)
+    B, S, H, D, N, Wc = 2, 1, 4, 32, 20, 8
+    q = rng.standard_normal((B, S, H, D))
+    cmp = rng.standard_normal((B, N, D))
+    win = rng.standard_normal((B, Wc, D))
+    sink = rng.standard_normal(H)
+    q_pos = np.array([200, 150], dtype=np.int32)
+    valid = np.array([[[3, 7, 11, 19]], [[0, 5, 6, 18]]], dtype=np.int32)
+    noisy = np.array([[[3, 20, 7, -1, 11, 99, 19, 2 ** 30]], [[-1, 0, 5, 20, 6, 18, 21, -7]]], dtype=np.int32)
+    a, la, na = orc.attn(q, cmp, win, sink, q_pos, topk_idx=valid, window=Wc, rope_dim=8)
+    b, lb, nb = orc.attn(q, cmp, win, sink, q_pos, topk_idx=noisy, window=Wc, rope_dim=8)
+    assert np.array_equal(na, nb)
+    np.testing.assert_allclose(b, a, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lb, la, rtol=0, atol=1e-12)

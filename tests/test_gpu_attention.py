@@ -182,3 +182,26 @@ def test_moving_maximum_and_short_contexts_32_heads(orc, dense, sink_inf):
     torch.cuda.synchronize()
     assert_close(to_np(out), ref, TOL["bf16"], f"moving max dense={dense} sink_inf={sink_inf}: output")
     assert_close(lse.cpu().numpy(), rlse, 1e-3, f"moving max dense={dense} sink_inf={sink_inf}: lse")
+
+
+@pytest.mark.parametrize("H,B", [(128, 16), (48, 3), (8, 2)])
+def test_list_entries_past_the_cache_are_skipped(orc, H, B):
+    """Top-k entries at or past N_cap (and negative ones other than -1) select
+    nothing, on the GPU as in the oracle (both head groupings and the generic
+    kernel)."""
+    N_cap, k = 500, 256
+    x = _inputs(41 + H, B, 1, H, N_cap, 128, k, [1999 - 37 * i for i in range(B)])
+    topk = x["topk"].copy()
+    rng = np.random.default_rng(H)
+    bad = rng.random(topk.shape) < 0.2
+    topk[bad] = rng.choice(np.array([N_cap, N_cap + 3, 2 ** 30, -7, -2 ** 31], dtype=np.int64),
+                           size=int(bad.sum())).astype(np.int32)
+    out = torch.empty((B, 1, H, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, 1, H), dtype=torch.float32, device="cuda")
+    print(f"[attn] out-of-range list entries H={H} B={B}", flush=True)
+    K.csa_sparse_attn(_dev(x["q"]), _dev(x["cmp"]), _dev(topk), _dev(x["win"]), None, _dev(x["sink"]),
+                      _dev(x["q_pos"]), out, lse, rope_dim=64, window=128)
+    torch.cuda.synchronize()
+    ref, rlse, _ = orc.attn(x["q"], x["cmp"], x["win"], x["sink"], x["q_pos"], topk_idx=topk, window=128, rope_dim=64)
+    assert_close(to_np(out), ref, TOL["bf16"], f"out-of-range entries H={H}: output")
+    assert_close(lse.cpu().numpy(), rlse, 1e-3, f"out-of-range entries H={H}: lse")

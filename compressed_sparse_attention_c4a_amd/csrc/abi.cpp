@@ -141,7 +141,7 @@ int csa_compress(const void* kv_state, const void* score_state, const float* gam
   REQ(ratio >= 1 && ratio <= 4096, "%s: ratio must be in [1, 4096]", fn);
   REQ(overlap == 0 || overlap == 1, "%s: overlap must be 0 or 1", fn);
   REQ(eps >= 0.f, "%s: eps must be >= 0", fn);
-  REQ((L + ratio - 1) / ratio + 1 <= 65535 * 1024, "%s: L too large", fn);
+  REQ(((long)L + ratio - 1) / ratio <= 65535L * 1024, "%s: L too large", fn);
   REQ(B <= 65535, "%s: B must be <= 65535", fn);
   const csa::CompressJob job{kv_state, score_state, gamma, cache, d, rope_dim, overlap, N_cap,
                              dtype == CSA_BF16_KV_FP8};
@@ -174,7 +174,7 @@ int csa_compress_kv_index(const void* kv_state, const void* score_state, const f
   REQ(ratio >= 1 && ratio <= 4096, "%s: ratio must be in [1, 4096]", fn);
   REQ(overlap == 0 || overlap == 1, "%s: overlap must be 0 or 1", fn);
   REQ(eps >= 0.f, "%s: eps must be >= 0", fn);
-  REQ((L + ratio - 1) / ratio + 1 <= 65535 * 1024, "%s: L too large", fn);
+  REQ(((long)L + ratio - 1) / ratio <= 65535L * 1024, "%s: L too large", fn);
   REQ(B <= 65535, "%s: B must be <= 65535", fn);
   const csa::CompressJob jobs[2] = {{kv_state, score_state, gamma, cache, d, rope_dim, overlap, N_cap,
                                      dtype == CSA_BF16_KV_FP8},
@@ -237,6 +237,7 @@ int csa_topk(const float* scores, const int32_t* q_pos, int32_t* topk_idx, float
 }
 
 size_t csa_index_topk_workspace_size(int B, int S, int N_cap, int k) {
+  if (B < 1 || S < 1 || N_cap < 1 || k < 1 || k > 4096) return 0;
   const size_t sc = ((size_t)B * S * N_cap * sizeof(float) + 255) & ~(size_t)255;
   return sc + csa_host::topk_workspace_size(B, S, N_cap, k);
 }
@@ -339,7 +340,7 @@ int csa_compress_index_topk(const void* kv_state, const void* score_state, const
   REQ(ratio <= 4096, "%s: ratio must be in [1, 4096]", fn);
   REQ(overlap == 0 || overlap == 1, "%s: overlap must be 0 or 1", fn);
   REQ(eps >= 0.f, "%s: eps must be >= 0", fn);
-  REQ((L + ratio - 1) / ratio + 1 <= 65535 * 1024, "%s: L too large", fn);
+  REQ(((long)L + ratio - 1) / ratio <= 65535L * 1024, "%s: L too large", fn);
   REQ(k >= 1 && k <= 4096, "%s: k must be in [1, 4096] (got %d)", fn, k);
   const size_t need = csa_index_topk_workspace_size(B, S, N_cap, k);
   if (!workspace || workspace_bytes < need)
@@ -383,7 +384,7 @@ int csa_sparse_attn(const void* q, const void* cmp_cache, const int32_t* topk_id
   REQ(k >= 0 && k <= 65536, "%s: k must be in [0, 65536]", fn);
   if (k > 0) REQ_PTR(topk_idx);
   if (dtype == CSA_BF16_KV_FP8 && k > 2048) return fail(CSA_ERR_UNSUPPORTED, "%s: FP8 KV rows need k <= 2048", fn);
-  const size_t need = csa_host::attn_workspace_size(B, S, H, D, window + k);
+  const size_t need = csa_host::attn_workspace_size(B, S, H, D, (long)window + k);
   if (need && (!workspace || workspace_bytes < need))
     return fail(CSA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed (got %zu)", fn, need, workspace_bytes);
   OPT_PTR(workspace);
@@ -401,7 +402,7 @@ int hca_attn(const void* q, const void* cmp_cache, const void* win_kv, const int
                                  N_cap, W_cap, window, dtype))
     return rc;
   REQ(ratio >= 1, "%s: ratio must be >= 1", fn);
-  const size_t need = csa_host::attn_workspace_size(B, S, H, D, window + N_cap);
+  const size_t need = csa_host::attn_workspace_size(B, S, H, D, (long)window + N_cap);
   if (need && (!workspace || workspace_bytes < need))
     return fail(CSA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed (got %zu)", fn, need, workspace_bytes);
   OPT_PTR(workspace);
@@ -467,7 +468,9 @@ int csa_pack_weights(const void* w, void* packed, int groups, int N, int K, csa_
 }
 
 size_t csa_q_proj_workspace_size(int M, int d_model, int q_rank, int H, int D) {
-  if (M < 1 || d_model < 512 || q_rank < 512 || H < 1 || D < 2) return 0;
+  if (M < 1 || M > (1 << 20) || d_model < 512 || d_model > (1 << 20) || q_rank < 512 || q_rank > 2048 || H < 1 ||
+      D < 2 || (long)H * D > (1 << 20))
+    return 0;  // outside what csa_q_proj accepts
   return max_sz(csa_host::gemm_partial_bytes(1, M, q_rank, d_model),
                 csa_host::gemm_partial_bytes(1, M, H * D, q_rank));
 }
@@ -484,7 +487,8 @@ int csa_q_proj(const void* x, const void* wq_a, const float* gamma_q, const void
   REQ_PTR(qr);
   REQ_PTR(q);
   REQ(B >= 1 && S >= 1 && (long)B * S <= (1 << 20), "%s: B*S must be in [1, 2^20]", fn);
-  REQ(d_model >= 512 && d_model % 512 == 0, "%s: d_model must be a positive multiple of 512", fn);
+  REQ(d_model >= 512 && d_model % 512 == 0 && d_model <= (1 << 20), "%s: d_model must be a multiple of 512 (<= 2^20)",
+      fn);
   REQ(q_rank >= 512 && q_rank % 512 == 0 && q_rank <= 2048, "%s: q_rank must be 512, 1024, 1536 or 2048", fn);
   REQ(H >= 1 && D >= 256 && D <= 2048 && D % 256 == 0, "%s: D must be a multiple of 256 in [256, 2048]", fn);
   REQ((long)H * D <= (1 << 20), "%s: H*D must be <= 2^20", fn);
@@ -519,7 +523,9 @@ static int finish_seg(int ncols) {
 }
 
 size_t csa_o_proj_workspace_size(int M, int H, int D, int groups, int o_rank, int d_model) {
-  if (M < 1 || H < 1 || D < 1 || groups < 1 || H % groups != 0 || o_rank < 1 || d_model < 1) return 0;
+  if (M < 1 || M > (1 << 20) || H < 1 || D < 1 || groups < 1 || H % groups != 0 || o_rank < 1 || d_model < 1 ||
+      d_model > (1 << 20) || (long)H * D > (1 << 20) || (long)groups * o_rank > (1 << 20))
+    return 0;  // outside what csa_o_proj accepts
   const int gdim = H / groups * D;
   return max_sz(csa_host::gemm_partial_bytes(groups, M, o_rank, gdim),
                 csa_host::gemm_partial_bytes(1, M, d_model, groups * o_rank));

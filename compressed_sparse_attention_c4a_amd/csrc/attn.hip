@@ -779,12 +779,12 @@ struct AttnPlan {
   size_t ws_bytes;
 };
 
-static AttnPlan attn_plan_nhb(long Q, int H, int n_cand, int nhb) {
+static AttnPlan attn_plan_nhb(long Q, int H, long n_cand, int nhb) {
   AttnPlan p;
   p.nhb = nhb;
   p.n_hg = H / (16 * p.nhb);
-  const long items = Q * p.n_hg;
-  const int nt = (n_cand + AT_TR - 1) / AT_TR;
+  const long items = Q * p.n_hg;  // >= 1: Q >= 1 and H >= 16 * nhb here
+  const long nt = (n_cand + AT_TR - 1) / AT_TR;
   // split the candidate tiles only when the items alone leave CUs idle, and
   // keep at least two tiles per split
   long ns = 1;
@@ -803,9 +803,9 @@ static AttnPlan attn_plan_nhb(long Q, int H, int n_cand, int nhb) {
 // MI355X at decode shapes (16 and 32 heads per workgroup over 3-18 tiles per
 // split, with and without splits): set-up 4.3 / 6.2 us, a 64-row tile 1.37 /
 // 1.75 us, the merge 4.7 us.
-static double attn_plan_cost(const AttnPlan& p, int n_cand) {
-  const int nt = (n_cand + AT_TR - 1) / AT_TR;
-  const int tps = (nt + p.nsplit - 1) / p.nsplit;
+static double attn_plan_cost(const AttnPlan& p, long n_cand) {
+  const long nt = (n_cand + AT_TR - 1) / AT_TR;
+  const long tps = (nt + p.nsplit - 1) / p.nsplit;
   const long rounds = (p.total + 255) / 256;
   const double setup = p.nhb == 2 ? 6.2 : 4.3, tile = p.nhb == 2 ? 1.75 : 1.37;
   return (double)rounds * (setup + tps * tile) + (p.nsplit > 1 ? 4.7 : 0.0);
@@ -817,15 +817,15 @@ static double attn_plan_cost(const AttnPlan& p, int n_cand) {
 // workgroups) and for long lists split twice (csa_decode_32k), 16 heads for
 // short lists at decode (hca_decode_32k, window-only layers: no split, no
 // merge) and for few queries (csa_decode_1m: 8 queries, 4 splits instead of 8).
-static AttnPlan attn_plan(long Q, int H, int n_cand) {
+static AttnPlan attn_plan(long Q, int H, long n_cand) {
   const AttnPlan p1 = attn_plan_nhb(Q, H, n_cand, 1);
   if (H % 32 != 0) return p1;
   const AttnPlan p2 = attn_plan_nhb(Q, H, n_cand, 2);
   return attn_plan_cost(p2, n_cand) <= attn_plan_cost(p1, n_cand) ? p2 : p1;
 }
 
-size_t attn_workspace_size(int B, int S, int H, int D, int n_cand) {
-  if (D != AT_D || H % 16 != 0) return 0;
+size_t attn_workspace_size(int B, int S, int H, int D, long n_cand) {
+  if (D != AT_D || H < 16 || H % 16 != 0 || B < 1 || S < 1 || n_cand < 0 || (long)B * S * H > INT32_MAX) return 0;
   return attn_plan((long)B * S, H, n_cand).ws_bytes;
 }
 
@@ -839,7 +839,7 @@ hipError_t launch_attn(const void* q, const void* cmp, const int32_t* topk_idx, 
   const long Q = (long)B * S;
   if ((dtype == CSA_BF16 || dtype == CSA_BF16_KV_FP8) && D == AT_D && H % 16 == 0 && (dense || k <= AT_MAXK) &&
       window <= AT_MAXWIN) {
-    const AttnPlan p = attn_plan(Q, H, window + (dense ? N_cap : k));
+    const AttnPlan p = attn_plan(Q, H, (long)window + (dense ? N_cap : k));
     float* part = p.nsplit > 1 ? (float*)ws : nullptr;
     const int items = p.total / p.nsplit;
     if (dtype == CSA_BF16_KV_FP8) {

@@ -284,7 +284,7 @@ hipError_t launch_index_scores_fused(const csa::FusedCompress& F, const void* q,
 size_t topk_workspace_size(int B, int S, int N_cap, int k);
 hipError_t launch_topk(const float* scores, const int32_t* q_pos, int32_t* idx, float* val, void* ws, int B, int S,
                        int N_cap, int k, int ratio, hipStream_t st, const csa::FusedCompress* F = nullptr);
-size_t attn_workspace_size(int B, int S, int H, int D, int n_cand);
+size_t attn_workspace_size(int B, int S, int H, int D, long n_cand);
 hipError_t launch_attn(const void* q, const void* cmp, const int32_t* topk_idx, int k, int dense, int ratio,
                        const void* win,
                        const int32_t* win_pos0, const float* sink, const int32_t* q_pos, void* out, float* lse,

@@ -332,6 +332,7 @@ static TopkPlan topk_plan(int N_cap, int k) {
 // Kept lists of the intermediate rounds: two ping-pong buffers of values and
 // indices, each sized for the first round's output.
 size_t topk_workspace_size(int B, int S, int N_cap, int k) {
+  if (B < 1 || S < 1 || N_cap < 1 || k < 1 || k > 4096) return 0;  // invalid shapes: the calls reject them
   const TopkPlan P = topk_plan(N_cap, k);
   if (P.rounds == 1) return 0;
   const size_t one = (size_t)B * S * P.nchunk[0] * k;

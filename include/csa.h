@@ -27,6 +27,7 @@
  *     outside the buffers instead of reading out of bounds.
  *   - Every pointer must be 16-byte aligned (CSA_ERR_ALIGN otherwise).
  *   - Calls are re-entrant: no state is kept between calls.
+ *   - The *_workspace_size functions return 0 for shapes their calls reject.
  */
 #ifndef CSA_H
 #define CSA_H

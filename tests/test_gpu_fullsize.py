@@ -32,16 +32,18 @@ def _run(inp):
     return dev, step, out
 
 
-@pytest.mark.parametrize("name", ["csa_decode_32k", "hca_decode_128k", "csa_decode_1m"])
+@pytest.mark.parametrize("name", ["csa_decode_32k", "hca_decode_128k", "csa_decode_1m", "hca_decode_32k",
+                                  "swa_decode_32k"])
 def test_decode_full_size(orc, name):
     sh = getattr(W, name)()
     inp = W.generate(sh)
     print(f"[fullsize] {name}: B={sh.B} N_cap={sh.N_cap}", flush=True)
     dev, step, out = _run(inp)
     ref = orc.pipeline(inp)
-    wr = ref["written"]
-    assert wr.any(), "the decode step completes a group and writes its entry"
-    assert_close(_rows(dev["cmp_cache"], wr), ref["cmp_vals"][wr], TOL["bf16"], f"{name}: compressed rows")
+    if not sh.swa:
+        wr = ref["written"]
+        assert wr.any(), "the decode step completes a group and writes its entry"
+        assert_close(_rows(dev["cmp_cache"], wr), ref["cmp_vals"][wr], TOL["bf16"], f"{name}: compressed rows")
     if sh.indexer:
         iw = ref["idx_written"]
         assert_close(_rows(dev["idx_cache"], iw), ref["idx_vals"][iw], TOL["bf16"], f"{name}: index-key rows")
